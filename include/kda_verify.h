@@ -1,0 +1,146 @@
+/*
+ * kda_verify.h - C ABI of the MI355X (gfx950) fused causal-conv1d + Kimi Delta
+ * Attention (KDA) multi-token verify-decode step.
+ *
+ * The operation is the one described on the cuLA pull request page "[KDA] Fuse
+ * causal conv1d into MTP verify decode #107" (PR description): a width-4 depthwise
+ * causal conv1d with SiLU over packed pre-convolution q/k/v activations, q/k L2
+ * normalisation, a per-channel decay gate (softplus or safe form) and a sigmoid
+ * beta, then the gated delta rule over T draft tokens with verify semantics:
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = S_t^T q_t,
+ *
+ * the persistent state S_{-1} is only read; each S_t goes to inter_ssm, each o_t to o;
+ * each token's raw conv window goes to conv_window, and conv_state is rolled in place
+ * to the last three raw tokens.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers (hipMalloc'd or from a caching allocator) unless
+ *     said otherwise. The caller owns every buffer; the library keeps no pointer
+ *     after a call returns and allocates no device memory.
+ *   - Arrays are dense, row-major and contiguous. Every device base pointer must be
+ *     16-byte aligned (KDA_ERR_ALIGN otherwise).
+ *   - Calls are asynchronous on `stream` (NULL = the default stream); none blocks the
+ *     host. A call that returns an error launched nothing and wrote nothing.
+ *   - No entry point throws; errors are returned as kda_status.
+ */
+#ifndef KDA_VERIFY_H
+#define KDA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent (e.g. HV % H != 0) */
+  KDA_ERR_UNSUPPORTED = -3, /* valid but not built: (K, V) pair, dtype, gate or variant */
+  KDA_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+  KDA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kda_workspace_bytes() */
+  KDA_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
+  KDA_ERR_ALIAS = -7        /* a written buffer overlaps another buffer */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Gate forms (PR#107 description: softplus gate and safe gate with a lower bound).
+ * With gamma = gate + dt_bias:
+ *   KDA_GATE_SOFTPLUS: log alpha = -exp(A_log) * softplus(gamma), where
+ *       softplus(x) = log(1 + exp(b x)) / b if b x <= threshold, else x
+ *       (a true branch; the exponential is never formed past the threshold,
+ *        PR#107 code review);
+ *   KDA_GATE_SAFE:     log alpha = lower_bound * sigmoid(exp(A_log) * gamma). */
+typedef enum { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE = 1 } kda_gate_mode;
+
+/* Kernel variant (PR#107 description: two variants, one API and one arithmetic).
+ * AUTO picks from N*HV and T; SMALL splits each value head's V columns over several
+ * workgroups; LARGE gives each (sequence, value head) one workgroup. Both variants
+ * return bit-identical results. */
+typedef enum { KDA_VARIANT_AUTO = 0, KDA_VARIANT_SMALL = 1, KDA_VARIANT_LARGE = 2 } kda_variant;
+
+typedef struct {
+  int32_t N;  /* sequences, >= 0 (N = 0 is a no-op) */
+  int32_t T;  /* draft tokens per sequence, 1 <= T <= KDA_MAX_T (any T >= 1, PR#107 commit 1) */
+  int32_t H;  /* q/k heads, >= 1 */
+  int32_t HV; /* value heads, a multiple of H; value head hv reads q/k head hv / (HV/H) */
+  int32_t K;  /* q/k head dim; (K, V) in {(16,16), (64,64), (128,128)} */
+  int32_t V;  /* value head dim */
+  int32_t in_dtype;  /* kda_dtype of mixed_qkv, conv_weight, conv_state, conv_window, gate, beta, o */
+  int32_t gate_mode; /* kda_gate_mode */
+  int32_t variant;   /* kda_variant */
+  float lower_bound;        /* safe gate bound, default -5.0 */
+  float softplus_beta;      /* default 1.0, must be > 0 */
+  float softplus_threshold; /* default 20.0 */
+  float scale;              /* q scale; <= 0 selects K^-1/2 */
+  float l2norm_eps;         /* q/k l2norm: x / sqrt(sum x^2 + eps); default 1e-6, >= 0 */
+} kda_verify_params;
+
+#define KDA_MAX_T 16
+
+/* Fill *p with the shape and the defaults above (AUTO variant, softplus gate, bf16). */
+void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t H, int32_t HV,
+                            int32_t K, int32_t V);
+
+/* Bytes of device workspace kda_conv_verify_decode needs for these params (one
+ * uint32 arrival counter per (sequence, q/k head), rounded up to 256). The counters
+ * decide which workgroup writes the q/k part of conv_state, which several
+ * workgroups read (PR#107 description: last-arrival counters). They must be zero
+ * before the first call (kda_workspace_reset); each call leaves them zero again.
+ * Returns 0 for invalid params. */
+size_t kda_workspace_bytes(const kda_verify_params* p);
+
+/* Zero `bytes` of workspace on `stream` with a fill kernel (graph-capturable). Use it
+ * once after allocation, and after a call that did not run to completion (PR#107 code
+ * review: stale counters would corrupt later calls). */
+kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream);
+
+/* The variant AUTO resolves to for these params (host-only, no HIP call), or a
+ * negative kda_status for invalid params. */
+int32_t kda_select_variant(const kda_verify_params* p);
+
+/* Validate params and pointers without launching (host-only, no HIP call). */
+kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
+                        const void* conv_state, const void* gate, const float* A_log,
+                        const float* dt_bias, const void* beta, const float* state, const void* o,
+                        const float* inter_ssm, const void* conv_window, const void* workspace,
+                        size_t workspace_bytes);
+
+/* One fused verify step (PR#107 description). C = 2*H*K + HV*V.
+ *   mixed_qkv   [N,T,C]      in_dtype, read.  Channels q (H*K) | k (H*K) | v (HV*V), head-major.
+ *   conv_weight [C,4]        in_dtype, read.  Tap 3 multiplies the newest token; no bias.
+ *   conv_state  [N,C,3]      in_dtype, read, then overwritten in place with the last three raw
+ *                            tokens of the extended sequence (old cache, then the T new tokens).
+ *   gate        [N,T,HV,K]   in_dtype, read.  Raw gate input.
+ *   A_log       [HV]         fp32, read.
+ *   dt_bias     [HV*K]       fp32, read.
+ *   beta        [N,T,HV]     in_dtype, read.  beta_t = sigmoid(beta).
+ *   state       [N,HV,K,V]   fp32, read only. Must not overlap inter_ssm.
+ *   o           [N,T,HV,V]   in_dtype, written (rounded to nearest even from fp32).
+ *   inter_ssm   [N,T,HV,K,V] fp32, written: the state after each token.
+ *   conv_window [N,T,C,3]    in_dtype, written: conv_window[n,t,c,:] is the conv cache to
+ *                            restore if tokens 0..t are accepted (bit copies of raw inputs).
+ *   workspace   >= kda_workspace_bytes(p) bytes, zeroed before first use; calls that
+ *               run at the same time need separate workspaces.
+ * q and k are L2-normalised per head after conv + SiLU, q is multiplied by `scale`;
+ * v is not normalised. Arithmetic is fp32; conv_window and conv_state are exact copies. */
+kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_qkv,
+                                  const void* conv_weight, void* conv_state, const void* gate,
+                                  const float* A_log, const float* dt_bias, const void* beta,
+                                  const float* state, void* o, float* inter_ssm, void* conv_window,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a kda_status value (never NULL). */
+const char* kda_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_VERIFY_H */

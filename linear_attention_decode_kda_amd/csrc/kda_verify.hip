@@ -1,0 +1,731 @@
+// Fused causal-conv1d + Kimi Delta Attention (KDA) multi-token verify step for
+// MI355X (gfx950, CDNA4), behind the C ABI of include/kda_verify.h.
+//
+// Operation: cuLA pull request page "[KDA] Fuse causal conv1d into MTP verify decode
+// #107" (PR description): width-4 depthwise causal conv1d + SiLU over packed q/k/v,
+// q/k L2 normalisation, softplus or safe decay gate, sigmoid beta, and the gated
+// delta rule over T draft tokens with verify semantics (state read only, every
+// token's state and conv window written, conv cache rolled in place).
+//
+// Design (our own, for gfx950; the page's CuTe kernels target NVIDIA parts):
+//   * One workgroup (WG) per (sequence n, value head hv, V-tile vt). NW wave64s per
+//     WG, each wave owns CPW consecutive V columns of the fp32 K x V state, held
+//     in VGPRs for all T tokens. Lane (kg, cg) holds 4 consecutive columns (one
+//     16-byte vector) of RPL consecutive rows.
+//   * Prologue: every input the WG needs besides the state (its q/k channels, its
+//     v-column channels, their conv cache and weights, the gate row, dt_bias, beta)
+//     is fetched with 16-byte loads into LDS; the 16-byte state loads are issued
+//     right behind them and stay in flight through the conv / gate / l2norm math,
+//     which all threads do from LDS.
+//   * Token loop: the decay is folded into the two K-reductions,
+//       u_j = sum_i (k_i a_i) S_ij,   w_j = sum_i (q_i a_i) S_ij,
+//       d_j = beta (v_j - u_j),       o_j = w_j + (q.k) d_j,
+//       S_ij <- a_i S_ij + k_i d_j,
+//     one pass over the registers for both sums, cross-lane sums with DPP and the
+//     gfx950 permlane16/32 swaps (no LDS round trip), then one pass to update and
+//     stream the snapshot out with 16-byte non-temporal stores.
+//   * K-sums use one fixed tree (sequential over blocks of 8 rows, then pairwise
+//     over blocks) in every variant, so the small and large variants are
+//     bit-identical.
+//   * The q/k part of conv_state is read by the g*NVT WGs of a (n, q/k head) group
+//     and must be overwritten only after all of them read it (PR#107 description:
+//     last-arrival counters). Each WG bumps a per-group counter once its reads have
+//     landed; the one that sees the final count writes and re-zeroes the counter.
+//     No WG ever waits on another.
+// No MFMA: each token is rank-1 updates and matrix-vector products, bound by HBM.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kda_verify.h"
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ----------------------------------------------------------------------------------
+// element types: raw storage of the input dtype (bf16 bits or fp32 bits)
+// ----------------------------------------------------------------------------------
+__device__ __forceinline__ float up(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float up(uint32_t x) { return __uint_as_float(x); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename R> struct OutVec;
+template <> struct OutVec<uint16_t> {
+  // 4 bf16 outputs -> one 8-byte store
+  static __device__ __forceinline__ void store(void* base, size_t idx, float a, float b, float c, float d) {
+    u32x2 v;
+    v.x = bf16_rne(a) | (bf16_rne(b) << 16);
+    v.y = bf16_rne(c) | (bf16_rne(d) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + idx) = v;
+  }
+};
+template <> struct OutVec<uint32_t> {
+  static __device__ __forceinline__ void store(void* base, size_t idx, float a, float b, float c, float d) {
+    f32x4 v = {a, b, c, d};
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx) = v;
+  }
+};
+
+// ----------------------------------------------------------------------------------
+// cross-lane all-reduce steps: x + x[lane ^ MASK], the same bits on both partners
+// ----------------------------------------------------------------------------------
+template <int MASK>
+__device__ __forceinline__ float xor_sum(float x) {
+  if constexpr (MASK == 32) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (MASK == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (MASK == 8) {  // row_ror:8 inside a 16-lane row is lane ^ 8
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  } else if constexpr (MASK == 4) {  // ds_swizzle bit mode: and 0x1f, xor 4
+    return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101f));
+  } else if constexpr (MASK == 2) {  // quad_perm [2,3,0,1]
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
+  } else {
+    static_assert(MASK == 1, "mask");  // quad_perm [1,0,3,2]
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+  }
+}
+
+// sum over the lanes that differ only in bits [log2(LO), 6) of the lane id
+template <int LO>
+__device__ __forceinline__ float lane_sum_from(float x) {
+  if constexpr (LO <= 1) x = xor_sum<1>(x);
+  if constexpr (LO <= 2) x = xor_sum<2>(x);
+  if constexpr (LO <= 4) x = xor_sum<4>(x);
+  if constexpr (LO <= 8) x = xor_sum<8>(x);
+  if constexpr (LO <= 16) x = xor_sum<16>(x);
+  if constexpr (LO <= 32) x = xor_sum<32>(x);
+  return x;
+}
+
+// ----------------------------------------------------------------------------------
+// kernel arguments
+// ----------------------------------------------------------------------------------
+struct Args {
+  const void* mixed_qkv;
+  const void* conv_weight;
+  void* conv_state;
+  const void* gate;
+  const float* A_log;
+  const float* dt_bias;
+  const void* beta;
+  const float* state;
+  void* o;
+  float* inter_ssm;
+  void* conv_window;
+  uint32_t* counters;
+  int N, T, H, HV, C;
+  int g;      // HV / H
+  int group;  // WGs reading one q/k head's conv cache: g * (V-tiles)
+  int gate_mode;
+  float lower_bound, softplus_beta, softplus_threshold, scale, eps;
+};
+
+template <typename R, int K_, int V_, int CPW_, int NW_, int TMAX_>
+struct Cfg {
+  static constexpr int K = K_, V = V_, CPW = CPW_, NW = NW_, TMAX = TMAX_;
+  static constexpr int NTHR = NW * 64;
+  static constexpr int VT = NW * CPW;  // V columns per WG
+  static constexpr int NVT = V / VT;   // WGs per (n, hv)
+  static constexpr int CG = CPW / 4;   // lanes across a wave's columns
+  static constexpr int KG = 64 / CG;   // lanes across K
+  static constexpr int RPL = K / KG;   // rows per lane
+  static constexpr int BR = RPL < 8 ? RPL : 8;  // rows per summation block
+  static constexpr int NB = RPL / BR;           // blocks per lane
+  static constexpr int NCH = 2 * K + VT;        // channels a WG stages: q, k, its v columns
+  static constexpr int E16 = 16 / (int)sizeof(R);  // elements per 16-byte vector
+  static constexpr int RSTRIDE = K + K / RPL;   // rows per token in LDS, one pad row per RPL
+  static_assert(V % VT == 0 && CPW % 4 == 0 && 64 % CG == 0 && K % KG == 0, "tile shape");
+  static_assert(NB * BR == RPL && (NB & (NB - 1)) == 0, "blocks");
+  static_assert(K % E16 == 0 && VT % E16 == 0 && K % 4 == 0 && K <= 128, "vector widths");
+  // 16-byte vectors staged per WG at T = TMAX
+  static constexpr int MAX_CHUNKS = TMAX * NCH / E16 + 3 * NCH / E16 + 4 * NCH / E16 + TMAX * K / E16 + K / 4;
+  static constexpr int MAXC = (MAX_CHUNKS + NTHR - 1) / NTHR;
+};
+
+template <class CF, typename R>
+struct alignas(16) Smem {
+  f32x4 row[CF::TMAX * CF::RSTRIDE];  // per token, per K row: {k*a, q*a, a, k} (q scaled)
+  float vs[CF::TMAX * CF::VT];        // SiLU(conv(v)) of the WG's columns
+  float betas[CF::TMAX];
+  float qk[CF::TMAX];
+  alignas(16) R xs[CF::TMAX * CF::NCH];  // raw new tokens, [t][local channel]
+  alignas(16) R cs[3 * CF::NCH];         // raw conv cache, [local channel][3]
+  alignas(16) R ws[4 * CF::NCH];         // conv taps, [local channel][4]
+  alignas(16) R gs[CF::TMAX * CF::K];    // raw gate, [t][K]
+  alignas(16) float dtb[CF::K];
+  R bs[CF::TMAX];
+  int last;
+};
+
+template <class CF>
+__device__ __forceinline__ int row_slot(int t, int i) {
+  return t * CF::RSTRIDE + i + i / CF::RPL;
+}
+
+// global channel of local staged channel lc (q block, k block, then this WG's v columns)
+template <class CF>
+__device__ __forceinline__ int gchan(int lc, int h, int H, int hv, int vt) {
+  if (lc < CF::K) return h * CF::K + lc;
+  if (lc < 2 * CF::K) return H * CF::K + h * CF::K + (lc - CF::K);
+  return 2 * H * CF::K + hv * CF::V + vt * CF::VT + (lc - 2 * CF::K);
+}
+
+// raw element e[tau] of local channel lc: the cache for tau < 3, then the new tokens
+template <class CF, typename R>
+__device__ __forceinline__ R ext_raw(const Smem<CF, R>& s, int lc, int tau) {
+  return tau < 3 ? s.cs[lc * 3 + tau] : s.xs[(tau - 3) * CF::NCH + lc];
+}
+
+// Write raw conv-window / conv-cache vectors of one channel segment from LDS.
+// seg_lc: first local channel; L: channels; tok < 0 selects the rolled cache (e[T..T+2]),
+// tok >= 0 the window of token tok (e[tok+1..tok+3]). m: 16-byte vector index.
+template <class CF, typename R>
+__device__ __forceinline__ void put_window_vec(const Smem<CF, R>& s, R* dst_base, int seg_lc, int tok,
+                                               int T, int m) {
+  R v[CF::E16];
+#pragma unroll
+  for (int u = 0; u < CF::E16; ++u) {
+    const int e = m * CF::E16 + u;
+    const int lc = seg_lc + e / 3;
+    const int j = e - (e / 3) * 3;
+    const int tau = (tok < 0 ? T : tok + 1) + j;
+    v[u] = ext_raw<CF, R>(s, lc, tau);
+  }
+  u32x4 pk;
+  if constexpr (sizeof(R) == 2) {
+    pk.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+    pk.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+    pk.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+    pk.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+  } else {
+    pk.x = v[0];
+    pk.y = v[1];
+    pk.z = v[2];
+    pk.w = v[3];
+  }
+  *reinterpret_cast<u32x4*>(dst_base + (size_t)m * CF::E16) = pk;
+}
+
+template <class CF, typename R>
+__global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
+  constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
+  constexpr int RPL = CF::RPL, CG = CF::CG, VT = CF::VT;
+  __shared__ Smem<CF, R> s;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int T = a.T, H = a.H, HV = a.HV, C = a.C;
+  const int vt = blockIdx.x % CF::NVT;
+  const int unit = blockIdx.x / CF::NVT;  // n * HV + hv
+  const int hv = unit % HV, n = unit / HV;
+  const int h = hv / a.g;
+
+  const R* __restrict__ xq = static_cast<const R*>(a.mixed_qkv);
+  const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
+  R* cstate = static_cast<R*>(a.conv_state);
+  const R* __restrict__ gq = static_cast<const R*>(a.gate);
+  const R* __restrict__ bq = static_cast<const R*>(a.beta);
+
+  // ---------------- prologue: issue every 16-byte load of the WG's small inputs
+  const int PA = NCH / E16;
+  const int nA = T * PA;              // new tokens
+  const int nB = 3 * NCH / E16;       // conv cache
+  const int nC = 4 * NCH / E16;       // conv taps
+  const int nD = T * K / E16;         // gate
+  const int nE = K / 4;               // dt_bias (fp32)
+  const int total = nA + nB + nC + nD + nE;
+  u32x4 vals[CF::MAXC];
+  int dsts[CF::MAXC];
+  char* lds = reinterpret_cast<char*>(&s);
+#pragma unroll
+  for (int k = 0; k < CF::MAXC; ++k) {
+    int ci = tid + k * NTHR;
+    dsts[k] = -1;
+    if (ci < total) {
+      const void* src;
+      int dst;
+      if (ci < nA) {
+        const int t = ci / PA, pe = (ci - t * PA) * E16;
+        src = xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt);
+        dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
+      } else if ((ci -= nA) < nB) {
+        const int e = ci * E16, lc = e / 3;
+        src = cstate + ((size_t)n * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
+        dst = (int)((char*)&s.cs[e] - lds);
+      } else if ((ci -= nB) < nC) {
+        const int e = ci * E16, lc = e / 4;
+        src = wq + (size_t)gchan<CF>(lc, h, H, hv, vt) * 4 + (e - lc * 4);
+        dst = (int)((char*)&s.ws[e] - lds);
+      } else if ((ci -= nC) < nD) {
+        const int e = ci * E16, t = e / K;
+        src = gq + ((size_t)(n * T + t) * HV + hv) * K + (e - t * K);
+        dst = (int)((char*)&s.gs[e] - lds);
+      } else {
+        ci -= nD;
+        src = a.dt_bias + (size_t)hv * K + ci * 4;
+        dst = (int)((char*)&s.dtb[ci * 4] - lds);
+      }
+      vals[k] = *reinterpret_cast<const u32x4*>(src);
+      dsts[k] = dst;
+    }
+  }
+  R bval = 0;
+  if (tid < T) bval = bq[(size_t)(n * T + tid) * HV + hv];
+
+  // ---------------- state tile: 16-byte loads, left in flight through the prologue math
+  const int cg = lane % CG, kg = lane / CG;
+  const int col = vt * VT + wave * CF::CPW + cg * 4;
+  const int row0 = kg * RPL;
+  const size_t KV = (size_t)K * V;
+  const float* sp = a.state + (size_t)unit * KV + (size_t)row0 * V + col;
+  f32x4 S[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)r * V));
+
+#pragma unroll
+  for (int k = 0; k < CF::MAXC; ++k)
+    if (dsts[k] >= 0) *reinterpret_cast<u32x4*>(lds + dsts[k]) = vals[k];
+  if (tid < T) s.bs[tid] = bval;
+  __syncthreads();  // B0: staged inputs visible; this WG's conv-cache reads have landed
+
+  // q/k conv-cache ownership: the last WG of the group to get here writes it
+  if (tid == 0) {
+    int last = 1;
+    if (a.group > 1) {
+      uint32_t* ctr = a.counters + (size_t)n * H + h;
+      const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev == (uint32_t)(a.group - 1);
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s.last = last;
+  }
+
+  // ---------------- phase 1a: conv + SiLU, one thread per staged channel, all tokens
+  for (int ch = tid; ch < NCH; ch += NTHR) {
+    const float w0 = up(s.ws[ch * 4 + 0]), w1 = up(s.ws[ch * 4 + 1]);
+    const float w2 = up(s.ws[ch * 4 + 2]), w3 = up(s.ws[ch * 4 + 3]);
+    float e0 = up(s.cs[ch * 3 + 0]), e1 = up(s.cs[ch * 3 + 1]), e2 = up(s.cs[ch * 3 + 2]);
+    for (int t = 0; t < T; ++t) {
+      const float x = up(s.xs[t * NCH + ch]);
+      const float y = fmaf(w3, x, fmaf(w2, e2, fmaf(w1, e1, w0 * e0)));
+      const float act = y / (1.0f + __expf(-y));
+      if (ch < K)
+        s.row[row_slot<CF>(t, ch)].y = act;  // q, normalised in phase 2
+      else if (ch < 2 * K)
+        s.row[row_slot<CF>(t, ch - K)].x = act;  // k
+      else
+        s.vs[t * VT + (ch - 2 * K)] = act;
+      e0 = e1;
+      e1 = e2;
+      e2 = x;
+    }
+  }
+
+  // ---------------- phase 1b: gate -> alpha, beta
+  {
+    const float eA = expf(a.A_log[hv]);
+    for (int gi = tid; gi < T * K; gi += NTHR) {
+      const int t = gi / K, i = gi - (gi / K) * K;
+      const float gam = up(s.gs[gi]) + s.dtb[i];
+      float ld;
+      if (a.gate_mode == KDA_GATE_SOFTPLUS) {
+        const float bx = a.softplus_beta * gam;
+        float sp;
+        if (bx <= a.softplus_threshold)
+          sp = log1pf(expf(bx)) / a.softplus_beta;
+        else
+          sp = gam;  // linear tail; the exponential is not formed here
+        ld = -eA * sp;
+      } else {
+        ld = a.lower_bound / (1.0f + expf(-eA * gam));
+      }
+      s.row[row_slot<CF>(t, i)].z = expf(ld);
+    }
+    if (tid < T) s.betas[tid] = 1.0f / (1.0f + expf(-up(s.bs[tid])));
+  }
+
+  // ---------------- phase 1c: conv windows (v columns always; q/k by one WG per group),
+  // rolled conv cache of the v columns (read only by this WG)
+  {
+    const bool qk_owner = (hv % a.g == 0) && vt == 0;
+    const int VQK = 3 * K / E16;  // vectors per token per q or k segment
+    const int VV = 3 * VT / E16;  // vectors per token of the v segment
+    const int nqk = qk_owner ? 2 * T * VQK : 0;
+    const int nv = T * VV;
+    const int nst = VV;
+    const int tot = nqk + nv + nst;
+    R* cw = static_cast<R*>(a.conv_window);
+    for (int q = tid; q < tot; q += NTHR) {
+      int seg_lc, tok, m;
+      if (q < nqk) {
+        const int seg = q / (T * VQK);
+        const int rem = q - seg * (T * VQK);
+        tok = rem / VQK;
+        m = rem - tok * VQK;
+        seg_lc = seg * K;
+      } else if (q < nqk + nv) {
+        const int rem = q - nqk;
+        tok = rem / VV;
+        m = rem - tok * VV;
+        seg_lc = 2 * K;
+      } else {
+        tok = -1;
+        m = q - nqk - nv;
+        seg_lc = 2 * K;
+      }
+      const int gc0 = gchan<CF>(seg_lc, h, H, hv, vt);
+      R* dst = tok < 0 ? cstate + ((size_t)n * C + gc0) * 3
+                       : cw + ((size_t)(n * T + tok) * C + gc0) * 3;
+      put_window_vec<CF, R>(s, dst, seg_lc, tok, T, m);
+    }
+  }
+  __syncthreads();  // B1
+
+  // ---------------- phase 2a: q/k l2norm per token (one wave per token), fold alpha in
+  for (int t = wave; t < T; t += CF::NW) {
+    float kx[2], qx[2];
+    float sk = 0.f, sq = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      kx[u] = qx[u] = 0.f;
+      if (i < K) {
+        const f32x4 r = s.row[row_slot<CF>(t, i)];
+        kx[u] = r.x;
+        qx[u] = r.y;
+      }
+      sk = fmaf(kx[u], kx[u], sk);
+      sq = fmaf(qx[u], qx[u], sq);
+      sqk = fmaf(qx[u], kx[u], sqk);
+    }
+    sk = lane_sum_from<1>(sk);
+    sq = lane_sum_from<1>(sq);
+    sqk = lane_sum_from<1>(sqk);
+    const float rk = 1.0f / sqrtf(sk + a.eps);
+    const float rq = a.scale / sqrtf(sq + a.eps);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      if (i < K) {
+        f32x4& r = s.row[row_slot<CF>(t, i)];
+        const float al = r.z;
+        const float kh = kx[u] * rk, qh = qx[u] * rq;
+        r = f32x4{kh * al, qh * al, al, kh};
+      }
+    }
+    if (lane == 0) s.qk[t] = sqk * rk * rq;
+  }
+
+  // ---------------- phase 2b: rolled conv cache of the q/k channels, by the last arriver
+  if (s.last) {
+    const int VQK = 3 * K / E16;
+    for (int q = tid; q < 2 * VQK; q += NTHR) {
+      const int seg = q / VQK, m = q - seg * VQK;
+      const int gc0 = gchan<CF>(seg * K, h, H, hv, vt);
+      put_window_vec<CF, R>(s, cstate + ((size_t)n * C + gc0) * 3, seg * K, -1, T, m);
+    }
+  }
+  __syncthreads();  // B2
+
+  // ---------------- token loop
+  float* snap = a.inter_ssm + (size_t)row0 * V + col;
+  const int rbase = kg * (RPL + 1);  // row_slot(t, row0) - t * RSTRIDE
+  for (int t = 0; t < T; ++t) {
+    const f32x4* rw = &s.row[t * CF::RSTRIDE + rbase];
+    // u = sum_i (k_i a_i) S_ij, w = sum_i (q_i a_i) S_ij over this lane's rows
+    float pu[CF::NB][4], pw[CF::NB][4];
+#pragma unroll
+    for (int b = 0; b < CF::NB; ++b) {
+#pragma unroll
+      for (int r = 0; r < CF::BR; ++r) {
+        const f32x4 rr = rw[b * CF::BR + r];
+        const f32x4 sv = S[b * CF::BR + r];
+        if (r == 0) {
+          pu[b][0] = rr.x * sv.x; pu[b][1] = rr.x * sv.y; pu[b][2] = rr.x * sv.z; pu[b][3] = rr.x * sv.w;
+          pw[b][0] = rr.y * sv.x; pw[b][1] = rr.y * sv.y; pw[b][2] = rr.y * sv.z; pw[b][3] = rr.y * sv.w;
+        } else {
+          pu[b][0] = fmaf(rr.x, sv.x, pu[b][0]); pu[b][1] = fmaf(rr.x, sv.y, pu[b][1]);
+          pu[b][2] = fmaf(rr.x, sv.z, pu[b][2]); pu[b][3] = fmaf(rr.x, sv.w, pu[b][3]);
+          pw[b][0] = fmaf(rr.y, sv.x, pw[b][0]); pw[b][1] = fmaf(rr.y, sv.y, pw[b][1]);
+          pw[b][2] = fmaf(rr.y, sv.z, pw[b][2]); pw[b][3] = fmaf(rr.y, sv.w, pw[b][3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 1; st < CF::NB; st *= 2)
+#pragma unroll
+      for (int b = 0; b < CF::NB; b += 2 * st)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pu[b][c] += pu[b + st][c];
+          pw[b][c] += pw[b + st][c];
+        }
+    float u[4], w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u[c] = lane_sum_from<CG>(pu[0][c]);
+      w[c] = lane_sum_from<CG>(pw[0][c]);
+    }
+    const f32x4 vv = *reinterpret_cast<const f32x4*>(&s.vs[t * VT + wave * CF::CPW + cg * 4]);
+    const float bt = s.betas[t], qk = s.qk[t];
+    float d[4];
+    d[0] = bt * (vv.x - u[0]);
+    d[1] = bt * (vv.y - u[1]);
+    d[2] = bt * (vv.z - u[2]);
+    d[3] = bt * (vv.w - u[3]);
+    const size_t nth = (size_t)(n * T + t) * HV + hv;
+    if (kg == 0)
+      OutVec<R>::store(a.o, nth * V + col, fmaf(qk, d[0], w[0]), fmaf(qk, d[1], w[1]),
+                       fmaf(qk, d[2], w[2]), fmaf(qk, d[3], w[3]));
+    // S_ij <- a_i S_ij + k_i d_j, then stream the snapshot out
+    float* dst = snap + nth * KV;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const f32x4 rr = rw[r];
+      f32x4 sv = S[r];
+      sv.x = fmaf(rr.z, sv.x, rr.w * d[0]);
+      sv.y = fmaf(rr.z, sv.y, rr.w * d[1]);
+      sv.z = fmaf(rr.z, sv.z, rr.w * d[2]);
+      sv.w = fmaf(rr.z, sv.w, rr.w * d[3]);
+      S[r] = sv;
+      __builtin_nontemporal_store(sv, reinterpret_cast<f32x4*>(dst + (size_t)r * V));
+    }
+  }
+}
+
+__global__ void zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// ----------------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------------
+using LaunchFn = hipError_t (*)(const Args&, hipStream_t);
+
+template <class CF, typename R>
+hipError_t launch(const Args& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((size_t)a.N * a.HV * CF::NVT);
+  Args copy = a;
+  copy.group = a.g * CF::NVT;
+  void* args[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_verify_kernel<CF, R>), dim3(grid),
+                         dim3(CF::NTHR), args, 0, stream);
+}
+
+// Tile shapes per (K, V) and variant. LARGE: one WG per (n, hv). SMALL: V split over
+// several WGs. For K = 128 both keep >= 8 rows per lane, so they share the K-sum tree.
+template <typename R, int TMAX>
+LaunchFn pick_tmax(int K, int V, int variant) {
+  if (K == 128 && V == 128) {
+    if (variant == KDA_VARIANT_LARGE) return &launch<Cfg<R, 128, 128, 32, 4, TMAX>, R>;
+    return &launch<Cfg<R, 128, 128, 16, 2, TMAX>, R>;
+  }
+  if (K == 64 && V == 64) {
+    if (variant == KDA_VARIANT_LARGE) return &launch<Cfg<R, 64, 64, 32, 2, TMAX>, R>;
+    return &launch<Cfg<R, 64, 64, 32, 1, TMAX>, R>;
+  }
+  if (K == 16 && V == 16) return &launch<Cfg<R, 16, 16, 16, 1, TMAX>, R>;
+  return nullptr;
+}
+
+template <typename R>
+LaunchFn pick(int K, int V, int variant, int T) {
+  if (T <= 4) return pick_tmax<R, 4>(K, V, variant);
+  if (T <= 8) return pick_tmax<R, 8>(K, V, variant);
+  return pick_tmax<R, 16>(K, V, variant);
+}
+
+bool supported_kv(int K, int V) { return K == V && (K == 16 || K == 64 || K == 128); }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t H, int32_t HV, int32_t K,
+                            int32_t V) {
+  if (!p) return;
+  memset(p, 0, sizeof(*p));
+  p->N = N;
+  p->T = T;
+  p->H = H;
+  p->HV = HV;
+  p->K = K;
+  p->V = V;
+  p->in_dtype = KDA_BF16;
+  p->gate_mode = KDA_GATE_SOFTPLUS;
+  p->variant = KDA_VARIANT_AUTO;
+  p->lower_bound = -5.0f;
+  p->softplus_beta = 1.0f;
+  p->softplus_threshold = 20.0f;
+  p->scale = 0.0f;
+  p->l2norm_eps = 1e-6f;
+}
+
+static kda_status check_params(const kda_verify_params* p) {
+  if (!p) return KDA_ERR_NULL;
+  if (p->N < 0 || p->T < 1 || p->T > KDA_MAX_T || p->H < 1 || p->HV < p->H || p->HV % p->H != 0 || p->K < 1 ||
+      p->V < 1)
+    return KDA_ERR_SHAPE;
+  const long long C = 2LL * p->H * p->K + (long long)p->HV * p->V;
+  if (C > 0x7fffffffLL || (long long)p->N * p->T * C > 0x7fffffffLL * 64LL) return KDA_ERR_SHAPE;
+  if ((long long)p->N * p->HV * 8 > 0x7fffffffLL) return KDA_ERR_SHAPE;
+  if ((long long)p->N * p->T > 0x7fffffffLL / 2) return KDA_ERR_SHAPE;
+  if (!supported_kv(p->K, p->V)) return KDA_ERR_UNSUPPORTED;
+  if (p->in_dtype != KDA_F32 && p->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE) return KDA_ERR_UNSUPPORTED;
+  if (p->variant < KDA_VARIANT_AUTO || p->variant > KDA_VARIANT_LARGE) return KDA_ERR_UNSUPPORTED;
+  if (!(p->softplus_beta > 0.0f) || !(p->l2norm_eps >= 0.0f) || p->scale != p->scale) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+size_t kda_workspace_bytes(const kda_verify_params* p) {
+  if (check_params(p) != KDA_OK) return 0;
+  size_t words = (size_t)p->N * p->H;
+  if (words == 0) words = 1;
+  return (words * 4 + 255) / 256 * 256;
+}
+
+int32_t kda_select_variant(const kda_verify_params* p) {
+  kda_status st = check_params(p);
+  if (st != KDA_OK) return st;
+  if (p->variant != KDA_VARIANT_AUTO) return p->variant;
+  if (p->K < 128) return KDA_VARIANT_LARGE;
+  // Fewer than ~4 WGs per CU of the 256-CU part: split V to raise the WG count.
+  const long long units = (long long)p->N * p->HV;
+  return units >= 1024 ? KDA_VARIANT_LARGE : KDA_VARIANT_SMALL;
+}
+
+kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
+                        const void* conv_state, const void* gate, const float* A_log, const float* dt_bias,
+                        const void* beta, const float* state, const void* o, const float* inter_ssm,
+                        const void* conv_window, const void* workspace, size_t workspace_bytes) {
+  kda_status st = check_params(p);
+  if (st != KDA_OK) return st;
+  if (p->N == 0) return KDA_OK;
+  const void* ptrs[] = {mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias,
+                        beta,      state,       o,          inter_ssm, conv_window, workspace};
+  for (const void* q : ptrs)
+    if (!q) return KDA_ERR_NULL;
+  for (const void* q : ptrs)
+    if (misaligned(q)) return KDA_ERR_ALIGN;
+  if (workspace_bytes < kda_workspace_bytes(p)) return KDA_ERR_WORKSPACE;
+
+  const size_t s = p->in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t N = p->N, T = p->T, HV = p->HV, K = p->K, V = p->V;
+  const size_t C = 2 * (size_t)p->H * K + HV * V;
+  auto rg = [](const void* q, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+    return Range{lo, lo + bytes};
+  };
+  const Range in[] = {rg(mixed_qkv, s * N * T * C), rg(conv_weight, s * C * 4), rg(gate, s * N * T * HV * K),
+                      rg(A_log, 4 * HV),            rg(dt_bias, 4 * HV * K),   rg(beta, s * N * T * HV),
+                      rg(state, 4 * N * HV * K * V)};
+  const Range out[] = {rg(conv_state, s * N * C * 3), rg(o, s * N * T * HV * V), rg(inter_ssm, 4 * N * T * HV * K * V),
+                       rg(conv_window, s * N * T * C * 3), rg(workspace, kda_workspace_bytes(p))};
+  // written buffers must not overlap each other or any read buffer
+  for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+    for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
+      if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return KDA_ERR_ALIAS;
+  }
+  return KDA_OK;
+}
+
+kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
+                                  void* conv_state, const void* gate, const float* A_log, const float* dt_bias,
+                                  const void* beta, const float* state, void* o, float* inter_ssm,
+                                  void* conv_window, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = kda_validate(p, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o,
+                               inter_ssm, conv_window, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  if (p->N == 0) return KDA_OK;
+  const int variant = kda_select_variant(p);
+  LaunchFn fn = p->in_dtype == KDA_BF16 ? pick<uint16_t>(p->K, p->V, variant, p->T)
+                                        : pick<uint32_t>(p->K, p->V, variant, p->T);
+  if (!fn) return KDA_ERR_UNSUPPORTED;
+  Args a;
+  a.mixed_qkv = mixed_qkv;
+  a.conv_weight = conv_weight;
+  a.conv_state = conv_state;
+  a.gate = gate;
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.inter_ssm = inter_ssm;
+  a.conv_window = conv_window;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.N = p->N;
+  a.T = p->T;
+  a.H = p->H;
+  a.HV = p->HV;
+  a.C = 2 * p->H * p->K + p->HV * p->V;
+  a.g = p->HV / p->H;
+  a.group = 0;
+  a.gate_mode = p->gate_mode;
+  a.lower_bound = p->lower_bound;
+  a.softplus_beta = p->softplus_beta;
+  a.softplus_threshold = p->softplus_threshold;
+  a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->K);
+  a.eps = p->l2norm_eps;
+  return fn(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return KDA_OK;
+  if (!workspace) return KDA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) || (bytes & 3u)) return KDA_ERR_ALIGN;
+  const size_t words = bytes / 4;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  uint32_t* wp = static_cast<uint32_t*>(workspace);
+  size_t n = words;
+  void* args[] = {&wp, &n};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&zero_words), dim3((unsigned)blocks), dim3(256), args, 0,
+                         stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+const char* kda_status_string(int32_t status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "unsupported (K, V), dtype, gate mode or variant";
+    case KDA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_ALIAS: return "an output buffer overlaps another buffer";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

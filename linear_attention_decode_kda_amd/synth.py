@@ -4,13 +4,15 @@ This module is shared by the CPU oracle's tests, the GPU parity tests and the
 benchmark. It holds no arithmetic of the method: it only draws random tensors of
 the right shapes and dtypes, and it names the workloads.
 
-Recipe (one fixed order so that every caller sees the same bits):
+Recipe (fixed, so that every caller sees the same bits whatever its thread count):
 
-* A CPU ``torch.Generator`` seeded with the workload's seed.
-* Draws, in this order, all in float32: mixed_qkv ~ N(0, 1), conv_weight ~ N(0, 0.5),
-  conv_state ~ N(0, 1), gate ~ N(0, 1), A_log ~ U(0, 1), dt_bias ~ N(0, 0.1),
-  beta ~ N(0, 1), state ~ N(0, 0.1). The second argument of N(., .) is read as the
-  standard deviation.
+* Tensors j = 0..7, in this order, all drawn in float32: mixed_qkv ~ N(0, 1),
+  conv_weight ~ N(0, 0.5), conv_state ~ N(0, 1), gate ~ N(0, 1), A_log ~ U(0, 1),
+  dt_bias ~ N(0, 0.1), beta ~ N(0, 1), state ~ N(0, 0.1). The second argument of
+  N(., .) is read as the standard deviation.
+* Each tensor is filled in chunks of 2**24 elements (row-major order); chunk i of
+  tensor j comes from its own CPU ``torch.Generator`` seeded with
+  (seed << 32) ^ (j << 24) ^ i. Chunks are drawn on a thread pool.
 * mixed_qkv, conv_weight, conv_state, gate and beta are then rounded to the input
   dtype (bf16 or fp32); A_log, dt_bias and state stay fp32.
 
@@ -21,6 +23,8 @@ page "[KDA] Fuse causal conv1d into MTP verify decode #107" (PR description).
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict
 
 import torch
@@ -80,22 +84,50 @@ L2NORM_EPS = 1e-6
 INPUT_NAMES = ("mixed_qkv", "conv_weight", "conv_state", "gate", "A_log", "dt_bias", "beta", "state")
 
 
+CHUNK = 1 << 24
+
+
+def _draw(shape, seed: int, j: int, kind: str, scale: float, pool: ThreadPoolExecutor) -> torch.Tensor:
+    n = 1
+    for d in shape:
+        n *= d
+    flat = torch.empty(n, dtype=torch.float32)
+
+    def fill(i: int) -> None:
+        g = torch.Generator(device="cpu")
+        g.manual_seed((seed << 32) ^ (j << 24) ^ i)
+        part = flat[i * CHUNK:min(n, (i + 1) * CHUNK)]
+        if kind == "normal":
+            torch.randn(part.numel(), generator=g, out=part)
+        else:
+            torch.rand(part.numel(), generator=g, out=part)
+
+    list(pool.map(fill, range((n + CHUNK - 1) // CHUNK)))
+    if scale != 1.0:
+        flat.mul_(scale)
+    return flat.view(shape)
+
+
 def make_inputs(w: Workload, seed: int | None = None) -> Dict[str, torch.Tensor]:
     """Draw one set of inputs for workload ``w`` on the CPU (see the module recipe)."""
-    g = torch.Generator(device="cpu")
-    g.manual_seed(w.seed if seed is None else seed)
-    N, T, H, HV, K, V, C = w.N, w.T, w.H, w.HV, w.K, w.V, w.C
+    seed = w.seed if seed is None else seed
+    N, T, HV, K, V, C = w.N, w.T, w.HV, w.K, w.V, w.C
     dt = w.torch_dtype
-    f32 = torch.float32
+    spec = [
+        ("mixed_qkv", (N, T, C), "normal", 1.0, dt),
+        ("conv_weight", (C, 4), "normal", 0.5, dt),
+        ("conv_state", (N, C, 3), "normal", 1.0, dt),
+        ("gate", (N, T, HV, K), "normal", 1.0, dt),
+        ("A_log", (HV,), "uniform", 1.0, torch.float32),
+        ("dt_bias", (HV * K,), "normal", 0.1, torch.float32),
+        ("beta", (N, T, HV), "normal", 1.0, dt),
+        ("state", (N, HV, K, V), "normal", 0.1, torch.float32),
+    ]
     out = {}
-    out["mixed_qkv"] = torch.randn((N, T, C), generator=g, dtype=f32).to(dt)
-    out["conv_weight"] = (torch.randn((C, 4), generator=g, dtype=f32) * 0.5).to(dt)
-    out["conv_state"] = torch.randn((N, C, 3), generator=g, dtype=f32).to(dt)
-    out["gate"] = torch.randn((N, T, HV, K), generator=g, dtype=f32).to(dt)
-    out["A_log"] = torch.rand((HV,), generator=g, dtype=f32)
-    out["dt_bias"] = torch.randn((HV * K,), generator=g, dtype=f32) * 0.1
-    out["beta"] = torch.randn((N, T, HV), generator=g, dtype=f32).to(dt)
-    out["state"] = torch.randn((N, HV, K, V), generator=g, dtype=f32) * 0.1
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as pool:
+        for j, (name, shape, kind, scale, odt) in enumerate(spec):
+            t = _draw(shape, seed, j, kind, scale, pool)
+            out[name] = t if odt == torch.float32 else t.to(odt)
     return out
 
 

@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI that run without a GPU.
+
+The library must load, export every function include/kda_verify.h declares, and
+reject every invalid argument before any HIP call. Pointers here are fake host
+integers: only validation runs, nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_decode_kda_amd as kda
+from linear_attention_decode_kda_amd import build as kbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if kbuild.is_stale():
+        kbuild.build()
+    return kda.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "kda_conv_verify_decode" in names and len(names) >= 7
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_params_init_defaults(lib):
+    p = kda.Params()
+    lib.kda_verify_params_init(ctypes.byref(p), 3, 4, 2, 4, 128, 128)
+    assert (p.N, p.T, p.H, p.HV, p.K, p.V) == (3, 4, 2, 4, 128, 128)
+    assert p.in_dtype == kda.BF16 and p.gate_mode == kda.GATE_SOFTPLUS and p.variant == kda.VARIANT_AUTO
+    assert p.lower_bound == -5.0 and p.softplus_beta == 1.0 and p.softplus_threshold == 20.0
+    assert p.scale == 0.0 and p.l2norm_eps == pytest.approx(1e-6)
+
+
+def test_workspace_bytes(lib):
+    assert kda.workspace_bytes(kda.make_params(256, 4, 32, 32, 128, 128)) == 256 * 32 * 4
+    assert kda.workspace_bytes(kda.make_params(3, 1, 2, 4, 128, 128)) == 256
+    assert kda.workspace_bytes(kda.make_params(3, 1, 2, 3, 128, 128)) == 0  # invalid: HV % H
+
+
+def test_select_variant(lib):
+    assert kda.select_variant(kda.make_params(256, 4, 32, 32, 128, 128)) == kda.VARIANT_LARGE
+    assert kda.select_variant(kda.make_params(32, 4, 16, 16, 128, 128)) == kda.VARIANT_SMALL
+    assert kda.select_variant(kda.make_params(2, 2, 2, 2, 16, 16)) == kda.VARIANT_LARGE
+    for v in (kda.VARIANT_SMALL, kda.VARIANT_LARGE):
+        assert kda.select_variant(kda.make_params(1, 1, 1, 1, 128, 128, variant=v)) == v
+    assert kda.select_variant(kda.make_params(1, 0, 1, 1, 128, 128)) == -2
+
+
+def _fake_ptrs(p, ws_bytes=None):
+    """Distinct, aligned, far-apart host integers standing in for device buffers."""
+    ptrs = [(i + 1) << 40 for i in range(12)]
+    return ptrs, (kda.workspace_bytes(p) if ws_bytes is None else ws_bytes)
+
+
+def _validate(lib, p, ptrs, ws_bytes):
+    return lib.kda_validate(ctypes.byref(p), *[ctypes.c_void_p(x) for x in ptrs], ws_bytes)
+
+
+def test_validate_accepts_good_args(lib):
+    for shape in [(256, 4, 32, 32, 128, 128), (2, 2, 2, 2, 16, 16), (3, 16, 1, 4, 64, 64)]:
+        p = kda.make_params(*shape)
+        ptrs, wsb = _fake_ptrs(p)
+        assert _validate(lib, p, ptrs, wsb) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("T", 0, -2), ("T", 17, -2), ("N", -1, -2), ("H", 0, -2), ("HV", 3, -2),
+    ("K", 32, -3), ("V", 64, -3), ("in_dtype", 7, -3), ("gate_mode", 2, -3), ("variant", 3, -3),
+    ("softplus_beta", 0.0, -2), ("l2norm_eps", -1.0, -2),
+])
+def test_validate_rejects_bad_params(lib, field, value, status):
+    p = kda.make_params(4, 4, 2, 4, 128, 128)
+    ptrs, wsb = _fake_ptrs(p)
+    setattr(p, field, value)
+    assert _validate(lib, p, ptrs, wsb) == status
+    # the launching entry point returns the same status without touching the GPU
+    assert lib.kda_conv_verify_decode(ctypes.byref(p), *[ctypes.c_void_p(x) for x in ptrs], wsb, None) == status
+
+
+def test_validate_pointer_errors(lib):
+    p = kda.make_params(4, 4, 2, 4, 128, 128)
+    ptrs, wsb = _fake_ptrs(p)
+    for i in range(12):
+        bad = list(ptrs)
+        bad[i] = 0
+        assert _validate(lib, p, bad, wsb) == -1, i
+        bad[i] = ptrs[i] + 4
+        assert _validate(lib, p, bad, wsb) == -4, i
+    assert _validate(lib, p, ptrs, wsb - 4) == -5
+    # an output overlapping an input or another output
+    for out_i in (2, 8, 9, 10, 11):
+        for other in range(12):
+            if other == out_i:
+                continue
+            bad = list(ptrs)
+            bad[out_i] = ptrs[other]
+            assert _validate(lib, p, bad, wsb) == -7, (out_i, other)
+    # inputs may alias each other (read only)
+    bad = list(ptrs)
+    bad[3] = ptrs[0]
+    assert _validate(lib, p, bad, wsb) == 0
+
+
+def test_zero_sequences_is_a_no_op(lib):
+    p = kda.make_params(0, 4, 2, 4, 128, 128)
+    null = [ctypes.c_void_p(0)] * 12
+    assert lib.kda_validate(ctypes.byref(p), *null, 0) == 0
+    assert lib.kda_conv_verify_decode(ctypes.byref(p), *null, 0, None) == 0
+
+
+def test_status_strings(lib):
+    for st in range(-7, 1):
+        s = lib.kda_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.kda_status_string(-99).decode() == "unknown status"
+
+
+def test_workspace_reset_argument_errors(lib):
+    assert lib.kda_workspace_reset(None, 0, None) == 0
+    assert lib.kda_workspace_reset(None, 256, None) == -1
+    assert lib.kda_workspace_reset(ctypes.c_void_p(1 << 40), 6, None) == -4
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        kda.load()
+
+
+def test_oracle_and_gpu_path_share_no_code():
+    """The oracle and the HIP library neither import nor include each other."""
+    pkg = os.path.join(ROOT, "linear_attention_decode_kda_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text and "kda_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "linear_attention_decode_kda_amd" not in text and "kda_verify" not in text, f
