@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # no packed-fp32 VALU forms in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep the one counter atomic a plain per-lane atomic: the wave-level rewrite reads
+    # its result at once, which stalls the wave on every load still in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

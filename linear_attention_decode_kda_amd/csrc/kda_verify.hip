@@ -8,10 +8,12 @@
 // token's state and conv window written, conv cache rolled in place).
 //
 // Design (our own, for gfx950; the page's CuTe kernels target NVIDIA parts):
-//   * One workgroup (WG) per (sequence n, value head hv, V-tile vt). NW wave64s per
-//     WG, each wave owns CPW consecutive V columns of the fp32 K x V state, held
-//     in VGPRs for all T tokens. Lane (kg, cg) holds 4 consecutive columns (one
-//     16-byte vector) of RPL consecutive rows.
+//   * One workgroup (WG) per (sequence n, value head hv, V-tile vt); the WG holds the
+//     fp32 K x VT state tile in VGPRs for all T tokens. Its NW wave64s split K: wave
+//     w owns rows [w*RW, (w+1)*RW). Inside a wave, LPR = VT/4 lanes span a row (one
+//     16-byte vector of 4 columns each) and Q = 64/LPR consecutive rows are covered
+//     by one instruction, so every state load and snapshot store of a wave moves
+//     64 x 16 contiguous bytes (two whole 512-byte rows when VT = 128).
 //   * Prologue: every input the WG needs besides the state (its q/k channels, its
 //     v-column channels, their conv cache and weights, the gate row, dt_bias, beta)
 //     is fetched with 16-byte loads into LDS; the 16-byte state loads are issued
@@ -22,10 +24,12 @@
 //       d_j = beta (v_j - u_j),       o_j = w_j + (q.k) d_j,
 //       S_ij <- a_i S_ij + k_i d_j,
 //     one pass over the registers for both sums, cross-lane sums with DPP and the
-//     gfx950 permlane16/32 swaps (no LDS round trip), then one pass to update and
-//     stream the snapshot out with 16-byte non-temporal stores.
-//   * K-sums use one fixed tree (sequential over blocks of 8 rows, then pairwise
-//     over blocks) in every variant, so the small and large variants are
+//     gfx950 permlane16/32 swaps, one small LDS exchange of per-wave partial sums
+//     (double-buffered, one barrier per token), then one pass to update and stream
+//     the snapshot out with 16-byte non-temporal stores.
+//   * K-sums follow one fixed tree in every tile shape (per wave: P partials of
+//     RW/P rows each summed in row order, then a fixed pairing order over the
+//     partials; then waves in index order), so the small and large variants are
 //     bit-identical.
 //   * The q/k part of conv_state is read by the g*NVT WGs of a (n, q/k head) group
 //     and must be overwritten only after all of them read it (PR#107 description:
@@ -112,6 +116,36 @@ __device__ __forceinline__ float lane_sum_from(float x) {
   return x;
 }
 
+// One 16-byte snapshot store with the chosen cache policy (vector memory only).
+template <int STP>
+__device__ __forceinline__ void store_snapshot(float* p, f32x4 v) {
+  if constexpr (STP == 1)
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  else
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+// x + x[lane ^ (LPR << bit)]; bit is a compile-time constant after unrolling
+template <int LPR>
+__device__ __forceinline__ float xor_sum_dyn(float x, int bit) {
+  const int mask = LPR << bit;
+  if (mask == 1) return xor_sum<1>(x);
+  if (mask == 2) return xor_sum<2>(x);
+  if (mask == 4) return xor_sum<4>(x);
+  if (mask == 8) return xor_sum<8>(x);
+  if (mask == 16) return xor_sum<16>(x);
+  return xor_sum<32>(x);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by blockIdx. Map blockIdx so that
+// each XCD works through one contiguous range of units: the WGs sharing an XCD's L2 then
+// stream through neighbouring state and snapshot addresses. A bijection on [0, B).
+__device__ __forceinline__ int xcd_order(int b, int B) {
+  constexpr int NXCD = 8;
+  const int x = b % NXCD, q = B / NXCD, r = B % NXCD;
+  return x * q + (x < r ? x : r) + b / NXCD;
+}
+
 // ----------------------------------------------------------------------------------
 // kernel arguments
 // ----------------------------------------------------------------------------------
@@ -135,32 +169,42 @@ struct Args {
   float lower_bound, softplus_beta, softplus_threshold, scale, eps;
 };
 
-template <typename R, int K_, int V_, int CPW_, int NW_, int TMAX_>
+// Snapshot store cache policy: streaming (nt) or agent-coherent write-through (sc1).
+enum StorePolicy { kStoreNT = 0, kStoreSC1 = 1 };
+
+template <typename R, int K_, int V_, int VT_, int NW_, int TMAX_, int STP_ = kStoreNT>
 struct Cfg {
-  static constexpr int K = K_, V = V_, CPW = CPW_, NW = NW_, TMAX = TMAX_;
+  static constexpr int K = K_, V = V_, VT = VT_, NW = NW_, TMAX = TMAX_, STP = STP_;
   static constexpr int NTHR = NW * 64;
-  static constexpr int VT = NW * CPW;  // V columns per WG
-  static constexpr int NVT = V / VT;   // WGs per (n, hv)
-  static constexpr int CG = CPW / 4;   // lanes across a wave's columns
-  static constexpr int KG = 64 / CG;   // lanes across K
-  static constexpr int RPL = K / KG;   // rows per lane
-  static constexpr int BR = RPL < 8 ? RPL : 8;  // rows per summation block
-  static constexpr int NB = RPL / BR;           // blocks per lane
+  static constexpr int NVT = V / VT;     // WGs per (n, hv)
+  static constexpr int RW = K / NW;      // K rows per wave
+  static constexpr int LPR = VT / 4;     // lanes across one row of the tile
+  static constexpr int Q = 64 / LPR;     // rows one wave instruction covers
+  static constexpr int RPL = RW / Q;     // rows per lane
+  static constexpr int P = K >= 64 ? 8 : 16;  // canonical partial sums per wave and column
+  static constexpr int M = P / Q;        // partials a lane holds
+  static constexpr int LOGQ = Q == 1 ? 0 : Q == 2 ? 1 : Q == 4 ? 2 : Q == 8 ? 3 : 4;
+  static constexpr int LOGP = P == 8 ? 3 : 4;
   static constexpr int NCH = 2 * K + VT;        // channels a WG stages: q, k, its v columns
   static constexpr int E16 = 16 / (int)sizeof(R);  // elements per 16-byte vector
-  static constexpr int RSTRIDE = K + K / RPL;   // rows per token in LDS, one pad row per RPL
-  static_assert(V % VT == 0 && CPW % 4 == 0 && 64 % CG == 0 && K % KG == 0, "tile shape");
-  static_assert(NB * BR == RPL && (NB & (NB - 1)) == 0, "blocks");
+  static_assert(V % VT == 0 && VT % 4 == 0 && 64 % LPR == 0 && K % NW == 0, "tile shape");
+  static_assert(RW % Q == 0 && P % Q == 0 && RPL % M == 0 && (1 << LOGQ) == Q && RW % P == 0, "rows");
   static_assert(K % E16 == 0 && VT % E16 == 0 && K % 4 == 0 && K <= 128, "vector widths");
   // 16-byte vectors staged per WG at T = TMAX
   static constexpr int MAX_CHUNKS = TMAX * NCH / E16 + 3 * NCH / E16 + 4 * NCH / E16 + TMAX * K / E16 + K / 4;
   static constexpr int MAXC = (MAX_CHUNKS + NTHR - 1) / NTHR;
 };
 
+// Pairing order of the P per-wave partial sums (bits of the partial index): the same
+// in every tile shape, so every variant forms the same sum.
+__device__ constexpr int kSumOrder8[3] = {1, 2, 0};
+__device__ constexpr int kSumOrder16[4] = {1, 2, 0, 3};
+
 template <class CF, typename R>
 struct alignas(16) Smem {
-  f32x4 row[CF::TMAX * CF::RSTRIDE];  // per token, per K row: {k*a, q*a, a, k} (q scaled)
+  f32x4 row[CF::TMAX * CF::K];        // per token, per K row: {k*a, q*a, a, k} (q scaled)
   float vs[CF::TMAX * CF::VT];        // SiLU(conv(v)) of the WG's columns
+  f32x4 part[2][CF::NW][2][CF::LPR];  // per-wave partial sums (u, w), double-buffered by token
   float betas[CF::TMAX];
   float qk[CF::TMAX];
   alignas(16) R xs[CF::TMAX * CF::NCH];  // raw new tokens, [t][local channel]
@@ -174,7 +218,7 @@ struct alignas(16) Smem {
 
 template <class CF>
 __device__ __forceinline__ int row_slot(int t, int i) {
-  return t * CF::RSTRIDE + i + i / CF::RPL;
+  return t * CF::K + i;
 }
 
 // global channel of local staged channel lc (q block, k block, then this WG's v columns)
@@ -224,14 +268,15 @@ __device__ __forceinline__ void put_window_vec(const Smem<CF, R>& s, R* dst_base
 template <class CF, typename R>
 __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
-  constexpr int RPL = CF::RPL, CG = CF::CG, VT = CF::VT;
+  constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
   __shared__ Smem<CF, R> s;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int T = a.T, H = a.H, HV = a.HV, C = a.C;
-  const int vt = blockIdx.x % CF::NVT;
-  const int unit = blockIdx.x / CF::NVT;  // n * HV + hv
+  const int lb = xcd_order(blockIdx.x, gridDim.x);
+  const int vt = lb % CF::NVT;
+  const int unit = lb / CF::NVT;  // n * HV + hv
   const int hv = unit % HV, n = unit / HV;
   const int h = hv / a.g;
 
@@ -252,50 +297,51 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   u32x4 vals[CF::MAXC];
   int dsts[CF::MAXC];
   char* lds = reinterpret_cast<char*>(&s);
+  const float alog = a.A_log[hv];
+  // Every slot loads unconditionally (a slot past the end re-reads the last vector and
+  // is not stored), so the loads issue back to back with no wait between them.
 #pragma unroll
   for (int k = 0; k < CF::MAXC; ++k) {
-    int ci = tid + k * NTHR;
-    dsts[k] = -1;
-    if (ci < total) {
-      const void* src;
-      int dst;
-      if (ci < nA) {
-        const int t = ci / PA, pe = (ci - t * PA) * E16;
-        src = xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt);
-        dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
-      } else if ((ci -= nA) < nB) {
-        const int e = ci * E16, lc = e / 3;
-        src = cstate + ((size_t)n * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
-        dst = (int)((char*)&s.cs[e] - lds);
-      } else if ((ci -= nB) < nC) {
-        const int e = ci * E16, lc = e / 4;
-        src = wq + (size_t)gchan<CF>(lc, h, H, hv, vt) * 4 + (e - lc * 4);
-        dst = (int)((char*)&s.ws[e] - lds);
-      } else if ((ci -= nC) < nD) {
-        const int e = ci * E16, t = e / K;
-        src = gq + ((size_t)(n * T + t) * HV + hv) * K + (e - t * K);
-        dst = (int)((char*)&s.gs[e] - lds);
-      } else {
-        ci -= nD;
-        src = a.dt_bias + (size_t)hv * K + ci * 4;
-        dst = (int)((char*)&s.dtb[ci * 4] - lds);
-      }
-      vals[k] = *reinterpret_cast<const u32x4*>(src);
-      dsts[k] = dst;
+    const int cv = tid + k * NTHR;
+    int ci = cv < total ? cv : total - 1;
+    const void* src;
+    int dst;
+    if (ci < nA) {
+      const int t = ci / PA, pe = (ci - t * PA) * E16;
+      src = xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt);
+      dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
+    } else if ((ci -= nA) < nB) {
+      const int e = ci * E16, lc = e / 3;
+      src = cstate + ((size_t)n * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
+      dst = (int)((char*)&s.cs[e] - lds);
+    } else if ((ci -= nB) < nC) {
+      const int e = ci * E16, lc = e / 4;
+      src = wq + (size_t)gchan<CF>(lc, h, H, hv, vt) * 4 + (e - lc * 4);
+      dst = (int)((char*)&s.ws[e] - lds);
+    } else if ((ci -= nC) < nD) {
+      const int e = ci * E16, t = e / K;
+      src = gq + ((size_t)(n * T + t) * HV + hv) * K + (e - t * K);
+      dst = (int)((char*)&s.gs[e] - lds);
+    } else {
+      ci -= nD;
+      src = a.dt_bias + (size_t)hv * K + ci * 4;
+      dst = (int)((char*)&s.dtb[ci * 4] - lds);
     }
+    vals[k] = *reinterpret_cast<const u32x4*>(src);
+    dsts[k] = cv < total ? dst : -1;
   }
-  R bval = 0;
-  if (tid < T) bval = bq[(size_t)(n * T + tid) * HV + hv];
+  const R bval = bq[(size_t)(n * T + (tid < T ? tid : T - 1)) * HV + hv];
 
   // ---------------- state tile: 16-byte loads, left in flight through the prologue math
-  const int cg = lane % CG, kg = lane / CG;
-  const int col = vt * VT + wave * CF::CPW + cg * 4;
-  const int row0 = kg * RPL;
+  const int c4 = lane % LPR, qq = lane / LPR;
+  const int col = vt * VT + c4 * 4;
+  const int row0 = wave * CF::RW + qq;  // this lane's rows: row0 + Q * r
   const size_t KV = (size_t)K * V;
   const float* sp = a.state + (size_t)unit * KV + (size_t)row0 * V + col;
   f32x4 S[RPL];
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)r * V));
+  for (int r = 0; r < RPL; ++r)
+    S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)r * Q * V));
 
 #pragma unroll
   for (int k = 0; k < CF::MAXC; ++k)
@@ -303,17 +349,11 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   if (tid < T) s.bs[tid] = bval;
   __syncthreads();  // B0: staged inputs visible; this WG's conv-cache reads have landed
 
-  // q/k conv-cache ownership: the last WG of the group to get here writes it
-  if (tid == 0) {
-    int last = 1;
-    if (a.group > 1) {
-      uint32_t* ctr = a.counters + (size_t)n * H + h;
-      const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = prev == (uint32_t)(a.group - 1);
-      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    s.last = last;
-  }
+  // q/k conv-cache ownership: count this WG in now (its reads have landed); the count
+  // is read only after the prologue math, so nothing waits on the atomic until then.
+  uint32_t prev = 0;
+  if (tid == 0 && a.group > 1)
+    prev = __hip_atomic_fetch_add(a.counters + (size_t)n * H + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---------------- phase 1a: conv + SiLU, one thread per staged channel, all tokens
   for (int ch = tid; ch < NCH; ch += NTHR) {
@@ -338,7 +378,7 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
 
   // ---------------- phase 1b: gate -> alpha, beta
   {
-    const float eA = expf(a.A_log[hv]);
+    const float eA = expf(alog);
     for (int gi = tid; gi < T * K; gi += NTHR) {
       const int t = gi / K, i = gi - (gi / K) * K;
       const float gam = up(s.gs[gi]) + s.dtb[i];
@@ -359,41 +399,6 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     if (tid < T) s.betas[tid] = 1.0f / (1.0f + expf(-up(s.bs[tid])));
   }
 
-  // ---------------- phase 1c: conv windows (v columns always; q/k by one WG per group),
-  // rolled conv cache of the v columns (read only by this WG)
-  {
-    const bool qk_owner = (hv % a.g == 0) && vt == 0;
-    const int VQK = 3 * K / E16;  // vectors per token per q or k segment
-    const int VV = 3 * VT / E16;  // vectors per token of the v segment
-    const int nqk = qk_owner ? 2 * T * VQK : 0;
-    const int nv = T * VV;
-    const int nst = VV;
-    const int tot = nqk + nv + nst;
-    R* cw = static_cast<R*>(a.conv_window);
-    for (int q = tid; q < tot; q += NTHR) {
-      int seg_lc, tok, m;
-      if (q < nqk) {
-        const int seg = q / (T * VQK);
-        const int rem = q - seg * (T * VQK);
-        tok = rem / VQK;
-        m = rem - tok * VQK;
-        seg_lc = seg * K;
-      } else if (q < nqk + nv) {
-        const int rem = q - nqk;
-        tok = rem / VV;
-        m = rem - tok * VV;
-        seg_lc = 2 * K;
-      } else {
-        tok = -1;
-        m = q - nqk - nv;
-        seg_lc = 2 * K;
-      }
-      const int gc0 = gchan<CF>(seg_lc, h, H, hv, vt);
-      R* dst = tok < 0 ? cstate + ((size_t)n * C + gc0) * 3
-                       : cw + ((size_t)(n * T + tok) * C + gc0) * 3;
-      put_window_vec<CF, R>(s, dst, seg_lc, tok, T, m);
-    }
-  }
   __syncthreads();  // B1
 
   // ---------------- phase 2a: q/k l2norm per token (one wave per token), fold alpha in
@@ -431,79 +436,149 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     if (lane == 0) s.qk[t] = sqk * rk * rq;
   }
 
-  // ---------------- phase 2b: rolled conv cache of the q/k channels, by the last arriver
-  if (s.last) {
-    const int VQK = 3 * K / E16;
-    for (int q = tid; q < 2 * VQK; q += NTHR) {
-      const int seg = q / VQK, m = q - seg * VQK;
-      const int gc0 = gchan<CF>(seg * K, h, H, hv, vt);
-      put_window_vec<CF, R>(s, cstate + ((size_t)n * C + gc0) * 3, seg * K, -1, T, m);
-    }
+  if (tid == 0) {
+    const bool last = a.group <= 1 || prev == (uint32_t)(a.group - 1);
+    if (last && a.group > 1)
+      __hip_atomic_store(a.counters + (size_t)n * H + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.last = last;
   }
   __syncthreads();  // B2
 
   // ---------------- token loop
   float* snap = a.inter_ssm + (size_t)row0 * V + col;
-  const int rbase = kg * (RPL + 1);  // row_slot(t, row0) - t * RSTRIDE
   for (int t = 0; t < T; ++t) {
-    const f32x4* rw = &s.row[t * CF::RSTRIDE + rbase];
-    // u = sum_i (k_i a_i) S_ij, w = sum_i (q_i a_i) S_ij over this lane's rows
-    float pu[CF::NB][4], pw[CF::NB][4];
+    const f32x4* rw = &s.row[t * K + row0];
+    // per-lane partials: rows row0 + Q*r, partial m = r % M, rows of a partial in order
+    float pu[M][4], pw[M][4];
 #pragma unroll
-    for (int b = 0; b < CF::NB; ++b) {
-#pragma unroll
-      for (int r = 0; r < CF::BR; ++r) {
-        const f32x4 rr = rw[b * CF::BR + r];
-        const f32x4 sv = S[b * CF::BR + r];
-        if (r == 0) {
-          pu[b][0] = rr.x * sv.x; pu[b][1] = rr.x * sv.y; pu[b][2] = rr.x * sv.z; pu[b][3] = rr.x * sv.w;
-          pw[b][0] = rr.y * sv.x; pw[b][1] = rr.y * sv.y; pw[b][2] = rr.y * sv.z; pw[b][3] = rr.y * sv.w;
-        } else {
-          pu[b][0] = fmaf(rr.x, sv.x, pu[b][0]); pu[b][1] = fmaf(rr.x, sv.y, pu[b][1]);
-          pu[b][2] = fmaf(rr.x, sv.z, pu[b][2]); pu[b][3] = fmaf(rr.x, sv.w, pu[b][3]);
-          pw[b][0] = fmaf(rr.y, sv.x, pw[b][0]); pw[b][1] = fmaf(rr.y, sv.y, pw[b][1]);
-          pw[b][2] = fmaf(rr.y, sv.z, pw[b][2]); pw[b][3] = fmaf(rr.y, sv.w, pw[b][3]);
-        }
+    for (int r = 0; r < RPL; ++r) {
+      const int m = r % M;
+      const f32x4 rr = rw[r * Q];
+      const f32x4 sv = S[r];
+      if (r < M) {
+        pu[m][0] = rr.x * sv.x; pu[m][1] = rr.x * sv.y; pu[m][2] = rr.x * sv.z; pu[m][3] = rr.x * sv.w;
+        pw[m][0] = rr.y * sv.x; pw[m][1] = rr.y * sv.y; pw[m][2] = rr.y * sv.z; pw[m][3] = rr.y * sv.w;
+      } else {
+        pu[m][0] = fmaf(rr.x, sv.x, pu[m][0]); pu[m][1] = fmaf(rr.x, sv.y, pu[m][1]);
+        pu[m][2] = fmaf(rr.x, sv.z, pu[m][2]); pu[m][3] = fmaf(rr.x, sv.w, pu[m][3]);
+        pw[m][0] = fmaf(rr.y, sv.x, pw[m][0]); pw[m][1] = fmaf(rr.y, sv.y, pw[m][1]);
+        pw[m][2] = fmaf(rr.y, sv.z, pw[m][2]); pw[m][3] = fmaf(rr.y, sv.w, pw[m][3]);
       }
     }
+    // the P partials of a column sit at index Q*m + qq; pair them in the fixed order
+    int done = 0;  // m bits already summed away (compile-time after unrolling)
 #pragma unroll
-    for (int st = 1; st < CF::NB; st *= 2)
+    for (int lv = 0; lv < CF::LOGP; ++lv) {
+      const int bit = CF::P == 8 ? kSumOrder8[lv] : kSumOrder16[lv];
+      if (bit >= CF::LOGQ) {  // both partners in this lane
+        const int mb = 1 << (bit - CF::LOGQ);
 #pragma unroll
-      for (int b = 0; b < CF::NB; b += 2 * st)
+        for (int m = 0; m < M; ++m)
+          if ((m & done) == 0 && (m & mb) == 0)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          pu[b][c] += pu[b + st][c];
-          pw[b][c] += pw[b + st][c];
-        }
-    float u[4], w[4];
+            for (int c = 0; c < 4; ++c) {
+              pu[m][c] += pu[m | mb][c];
+              pw[m][c] += pw[m | mb][c];
+            }
+        done |= mb;
+      } else {  // partner in lane ^ (LPR << bit)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u[c] = lane_sum_from<CG>(pu[0][c]);
-      w[c] = lane_sum_from<CG>(pw[0][c]);
+        for (int m = 0; m < M; ++m)
+          if ((m & done) == 0)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              pu[m][c] = xor_sum_dyn<LPR>(pu[m][c], bit);
+              pw[m][c] = xor_sum_dyn<LPR>(pw[m][c], bit);
+            }
+      }
     }
-    const f32x4 vv = *reinterpret_cast<const f32x4*>(&s.vs[t * VT + wave * CF::CPW + cg * 4]);
+    // wave partials through LDS, then waves summed in index order
+    const int buf = t & 1;
+    if (qq == 0) {
+      s.part[buf][wave][0][c4] = f32x4{pu[0][0], pu[0][1], pu[0][2], pu[0][3]};
+      s.part[buf][wave][1][c4] = f32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
+    }
+    __syncthreads();
+    f32x4 uu = s.part[buf][0][0][c4], ww = s.part[buf][0][1][c4];
+    if constexpr (CF::NW == 2) {
+      uu += s.part[buf][1][0][c4];
+      ww += s.part[buf][1][1][c4];
+    } else if constexpr (CF::NW == 4) {
+      uu = (uu + s.part[buf][1][0][c4]) + (s.part[buf][2][0][c4] + s.part[buf][3][0][c4]);
+      ww = (ww + s.part[buf][1][1][c4]) + (s.part[buf][2][1][c4] + s.part[buf][3][1][c4]);
+    } else {
+      static_assert(CF::NW == 1, "waves per WG");
+    }
+    const f32x4 vv = *reinterpret_cast<const f32x4*>(&s.vs[t * VT + c4 * 4]);
     const float bt = s.betas[t], qk = s.qk[t];
     float d[4];
-    d[0] = bt * (vv.x - u[0]);
-    d[1] = bt * (vv.y - u[1]);
-    d[2] = bt * (vv.z - u[2]);
-    d[3] = bt * (vv.w - u[3]);
+    d[0] = bt * (vv.x - uu.x);
+    d[1] = bt * (vv.y - uu.y);
+    d[2] = bt * (vv.z - uu.z);
+    d[3] = bt * (vv.w - uu.w);
     const size_t nth = (size_t)(n * T + t) * HV + hv;
-    if (kg == 0)
-      OutVec<R>::store(a.o, nth * V + col, fmaf(qk, d[0], w[0]), fmaf(qk, d[1], w[1]),
-                       fmaf(qk, d[2], w[2]), fmaf(qk, d[3], w[3]));
+    if (wave == 0 && qq == 0)
+      OutVec<R>::store(a.o, nth * V + col, fmaf(qk, d[0], ww.x), fmaf(qk, d[1], ww.y),
+                       fmaf(qk, d[2], ww.z), fmaf(qk, d[3], ww.w));
     // S_ij <- a_i S_ij + k_i d_j, then stream the snapshot out
     float* dst = snap + nth * KV;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const f32x4 rr = rw[r];
+      const f32x4 rr = rw[r * Q];
       f32x4 sv = S[r];
       sv.x = fmaf(rr.z, sv.x, rr.w * d[0]);
       sv.y = fmaf(rr.z, sv.y, rr.w * d[1]);
       sv.z = fmaf(rr.z, sv.z, rr.w * d[2]);
       sv.w = fmaf(rr.z, sv.w, rr.w * d[3]);
       S[r] = sv;
-      __builtin_nontemporal_store(sv, reinterpret_cast<f32x4*>(dst + (size_t)r * V));
+      store_snapshot<CF::STP>(dst + (size_t)r * Q * V, sv);
+    }
+  }
+
+  // ---------------- raw copies, issued last so that no wait for them ever precedes the
+  // token loop: conv windows (v columns always; q/k by one WG per group), the rolled
+  // conv cache of the v columns (read only by this WG), and the rolled cache of the
+  // shared q/k channels by the last WG of the group to count in (every other WG of the
+  // group counted itself only after its reads had landed)
+  {
+    const bool qk_owner = (hv % a.g == 0) && vt == 0;
+    const int VQK = 3 * K / E16;  // vectors per token per q or k segment
+    const int VV = 3 * VT / E16;  // vectors per token of the v segment
+    const int nqk = qk_owner ? 2 * T * VQK : 0;
+    const int nv = T * VV;
+    const int nst = VV;
+    const int tot = nqk + nv + nst;
+    R* cw = static_cast<R*>(a.conv_window);
+    for (int q = tid; q < tot; q += NTHR) {
+      int seg_lc, tok, m;
+      if (q < nqk) {
+        const int seg = q / (T * VQK);
+        const int rem = q - seg * (T * VQK);
+        tok = rem / VQK;
+        m = rem - tok * VQK;
+        seg_lc = seg * K;
+      } else if (q < nqk + nv) {
+        const int rem = q - nqk;
+        tok = rem / VV;
+        m = rem - tok * VV;
+        seg_lc = 2 * K;
+      } else {
+        tok = -1;
+        m = q - nqk - nv;
+        seg_lc = 2 * K;
+      }
+      const int gc0 = gchan<CF>(seg_lc, h, H, hv, vt);
+      R* dst = tok < 0 ? cstate + ((size_t)n * C + gc0) * 3
+                       : cw + ((size_t)(n * T + tok) * C + gc0) * 3;
+      put_window_vec<CF, R>(s, dst, seg_lc, tok, T, m);
+    }
+  }
+  if (s.last) {
+    constexpr int VQK = 3 * K / E16;
+    for (int q = tid; q < 2 * VQK; q += NTHR) {
+      const int seg = q / VQK, m = q - seg * VQK;
+      const int gc0 = gchan<CF>(seg * K, h, H, hv, vt);
+      put_window_vec<CF, R>(s, cstate + ((size_t)n * C + gc0) * 3, seg * K, -1, T, m);
     }
   }
 }
@@ -528,27 +603,58 @@ hipError_t launch(const Args& a, hipStream_t stream) {
                          dim3(CF::NTHR), args, 0, stream);
 }
 
-// Tile shapes per (K, V) and variant. LARGE: one WG per (n, hv). SMALL: V split over
-// several WGs. For K = 128 both keep >= 8 rows per lane, so they share the K-sum tree.
-template <typename R, int TMAX>
-LaunchFn pick_tmax(int K, int V, int variant) {
+// Tile shape and store policy per (K, V), variant and workload, measured on MI355X with
+// the fused step's own traffic (about 1 byte read per 4 written at T = 4):
+//   LARGE: one WG per (n, hv) covering all V columns.
+//   SMALL: V split over several WGs; more, shorter WGs shrink the tail of big grids and
+//          fill the chip for small ones.
+//   agent-coherent (sc1) snapshot stores win when snapshots dominate even more (T >= 8)
+//   or the whole working set stays in the 256 MB last-level cache (small batches);
+//   streaming (nt) stores win otherwise.
+// Every shape uses the same K split (32 rows per wave) and the same partial-sum tree,
+// so all of them return bit-identical results.
+struct Tile {
+  int vt;   // V columns per WG
+  int stp;  // StorePolicy
+};
+
+Tile choose_tile(int K, int V, int variant, int N, int T, int HV) {
+  const long long units = (long long)N * HV;
   if (K == 128 && V == 128) {
-    if (variant == KDA_VARIANT_LARGE) return &launch<Cfg<R, 128, 128, 32, 4, TMAX>, R>;
-    return &launch<Cfg<R, 128, 128, 16, 2, TMAX>, R>;
+    const bool small_ws = units < 1024;
+    const int stp = (T >= 8 || small_ws) ? kStoreSC1 : kStoreNT;
+    if (variant == KDA_VARIANT_LARGE) return {128, stp};
+    return {small_ws ? 64 : 32, stp};
+  }
+  if (K == 64 && V == 64) return {variant == KDA_VARIANT_LARGE ? 64 : 32, kStoreNT};
+  return {16, kStoreNT};
+}
+
+template <typename R, int TMAX>
+LaunchFn pick_tmax(int K, int V, Tile tl) {
+  if (K == 128 && V == 128) {
+    if (tl.vt == 128)
+      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1>, R>
+                                 : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT>, R>;
+    if (tl.vt == 64)
+      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1>, R>
+                                 : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT>, R>;
+    return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreSC1>, R>
+                               : &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNT>, R>;
   }
   if (K == 64 && V == 64) {
-    if (variant == KDA_VARIANT_LARGE) return &launch<Cfg<R, 64, 64, 32, 2, TMAX>, R>;
-    return &launch<Cfg<R, 64, 64, 32, 1, TMAX>, R>;
+    if (tl.vt == 64) return &launch<Cfg<R, 64, 64, 64, 2, TMAX>, R>;
+    return &launch<Cfg<R, 64, 64, 32, 2, TMAX>, R>;
   }
   if (K == 16 && V == 16) return &launch<Cfg<R, 16, 16, 16, 1, TMAX>, R>;
   return nullptr;
 }
 
 template <typename R>
-LaunchFn pick(int K, int V, int variant, int T) {
-  if (T <= 4) return pick_tmax<R, 4>(K, V, variant);
-  if (T <= 8) return pick_tmax<R, 8>(K, V, variant);
-  return pick_tmax<R, 16>(K, V, variant);
+LaunchFn pick(int K, int V, Tile tl, int T) {
+  if (T <= 4) return pick_tmax<R, 4>(K, V, tl);
+  if (T <= 8) return pick_tmax<R, 8>(K, V, tl);
+  return pick_tmax<R, 16>(K, V, tl);
 }
 
 bool supported_kv(int K, int V) { return K == V && (K == 16 || K == 64 || K == 128); }
@@ -615,9 +721,14 @@ int32_t kda_select_variant(const kda_verify_params* p) {
   if (st != KDA_OK) return st;
   if (p->variant != KDA_VARIANT_AUTO) return p->variant;
   if (p->K < 128) return KDA_VARIANT_LARGE;
-  // Fewer than ~4 WGs per CU of the 256-CU part: split V to raise the WG count.
+  // Crossovers measured on MI355X (K = V = 128): below 1024 (sequence, value head)
+  // units a whole-V WG per unit leaves CUs idle, so V is split; at T >= 8 the long
+  // write phase favours whole-V WGs; from 4096 units at T < 8 the shorter split WGs
+  // trim the tail of the grid.
   const long long units = (long long)p->N * p->HV;
-  return units >= 1024 ? KDA_VARIANT_LARGE : KDA_VARIANT_SMALL;
+  if (units < 1024) return KDA_VARIANT_SMALL;
+  if (p->T >= 8) return KDA_VARIANT_LARGE;
+  return units >= 4096 ? KDA_VARIANT_SMALL : KDA_VARIANT_LARGE;
 }
 
 kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
@@ -665,9 +776,9 @@ kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_
                                inter_ssm, conv_window, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
   if (p->N == 0) return KDA_OK;
-  const int variant = kda_select_variant(p);
-  LaunchFn fn = p->in_dtype == KDA_BF16 ? pick<uint16_t>(p->K, p->V, variant, p->T)
-                                        : pick<uint32_t>(p->K, p->V, variant, p->T);
+  const Tile tl = choose_tile(p->K, p->V, kda_select_variant(p), p->N, p->T, p->HV);
+  LaunchFn fn = p->in_dtype == KDA_BF16 ? pick<uint16_t>(p->K, p->V, tl, p->T)
+                                        : pick<uint32_t>(p->K, p->V, tl, p->T);
   if (!fn) return KDA_ERR_UNSUPPORTED;
   Args a;
   a.mixed_qkv = mixed_qkv;

@@ -53,8 +53,10 @@ def test_workspace_bytes(lib):
 
 
 def test_select_variant(lib):
-    assert kda.select_variant(kda.make_params(256, 4, 32, 32, 128, 128)) == kda.VARIANT_LARGE
+    assert kda.select_variant(kda.make_params(256, 4, 32, 32, 128, 128)) == kda.VARIANT_SMALL
     assert kda.select_variant(kda.make_params(32, 4, 16, 16, 128, 128)) == kda.VARIANT_SMALL
+    assert kda.select_variant(kda.make_params(64, 3, 16, 32, 128, 128)) == kda.VARIANT_LARGE
+    assert kda.select_variant(kda.make_params(512, 8, 16, 64, 128, 128)) == kda.VARIANT_LARGE
     assert kda.select_variant(kda.make_params(2, 2, 2, 2, 16, 16)) == kda.VARIANT_LARGE
     for v in (kda.VARIANT_SMALL, kda.VARIANT_LARGE):
         assert kda.select_variant(kda.make_params(1, 1, 1, 1, 128, 128, variant=v)) == v

@@ -229,3 +229,19 @@ def test_zero_q_k_channels():
     got = run_gpu(w, inp)
     assert_matches(w, got, oracle.verify_workload(w, inp), what="zero q/k")
     assert torch.count_nonzero(got["o"]) == 0
+
+
+@pytest.mark.parametrize("w", [W(64, 2, 64, 64, 128, 128, gate="safe"),   # 4096 units: split V in 32-column WGs
+                               W(16, 3, 8, 16, 128, 128),                  # 256 units: 64-column WGs, sc1 stores
+                               W(32, 8, 16, 32, 128, 128, gate="safe")])   # T = 8: sc1 stores in both variants
+def test_every_tile_shape_bit_identical(w):
+    """Whatever tile shape and store policy dispatch picks, the results are the same bits;
+    a sample of sequences is also checked against the oracle."""
+    inp = synth.make_inputs(w)
+    a = run_gpu(w, inp, S)
+    b = run_gpu(w, inp, L)
+    for k in ("o", "inter_ssm", "conv_window", "conv_state"):
+        assert torch.equal(a[k], b[k]), k
+    sample = np.array([0, w.N - 1])
+    ref = oracle.verify_workload(w.with_(N=2), slice_inputs(inp, sample))
+    assert_matches(w, a, ref, n_index=sample, what=f"tile shapes {w.name}")
