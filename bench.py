@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_batch")
     ap.add_argument("--variant", default="auto", choices=["auto", "small", "large"])
+    ap.add_argument("--op", default="verify", choices=["verify", "verify_pooled", "commit"],
+                    help="verify (the headline), verify on pooled buffers with scattered rows, or the accept step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -125,8 +127,42 @@ def main():
     ws = kda.alloc_workspace(p, dev)
     stream = torch.cuda.current_stream()
 
+    if args.op == "verify":
+        def step():
+            kda.run(p, inp, out, ws, stream)
+        b_alg = synth.algorithmic_bytes(w)
+    else:
+        # pools twice the batch, sequence rows scattered by a seeded permutation
+        g = torch.Generator().manual_seed(w.seed)
+        slots = 2 * w.N
+        idx = {k: torch.randperm(slots, generator=g)[: w.N].to(torch.int32).to(dev)
+               for k in ("cs", "st", "in")}
+        pools = kda.make_pools(w.N, idx["cs"], idx["st"], idx["in"], slots, slots, slots)
+        cs_pool = torch.zeros((slots, w.C, 3), dtype=w.torch_dtype, device=dev)
+        st_pool = torch.zeros((slots, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+        cs_pool[idx["cs"].long()] = inp["conv_state"]
+        st_pool[idx["st"].long()] = inp["state"]
+        is_pool = torch.zeros((slots, w.T, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+        cw_pool = torch.zeros((slots, w.T, w.C, 3), dtype=w.torch_dtype, device=dev)
+
+        def verify_pooled():
+            kda.kda_conv_verify_decode_pooled(p, pools, inp["mixed_qkv"], inp["conv_weight"], cs_pool, inp["gate"],
+                                              inp["A_log"], inp["dt_bias"], inp["beta"], st_pool, out["o"],
+                                              is_pool, cw_pool, ws, stream)
+        if args.op == "verify_pooled":
+            step = verify_pooled
+            b_alg = synth.algorithmic_bytes(w) + 3 * 4 * w.N
+        else:
+            verify_pooled()
+            acc = (torch.arange(w.N, dtype=torch.int32) % w.T + 1).to(dev)
+
+            def step():
+                kda.verify_commit(p, pools, acc, is_pool, cw_pool, st_pool, cs_pool, stream)
+            s_in = 2 if w.dtype == "bf16" else 4
+            b_alg = w.N * (2 * 4 * w.HV * w.K * w.V + 2 * 3 * s_in * w.C) + 4 * 4 * w.N
+
     for _ in range(args.warmup):
-        kda.run(p, inp, out, ws, stream)
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -135,7 +171,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        kda.run(p, inp, out, ws, stream)
+        step()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -144,16 +180,15 @@ def main():
     avg_kernel_s = sum(kern_ms) / len(kern_ms) / 1e3
     ms_per_step = wall * 1e3 / K
     tokens = w.N * w.T
-    b_alg = synth.algorithmic_bytes(w)
     achieved = b_alg / avg_kernel_s / 1e9
     print(f"[bench] {K} steps: wall {ms_per_step:.4f} ms/step, events {region_ms / K:.4f} ms/step, "
           f"kernel avg {avg_kernel_s * 1e3:.4f} ms min {min(kern_ms):.4f} max {max(kern_ms):.4f}; "
           f"{achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}",
           file=sys.stderr, flush=True)
 
-    traffic = measured_traffic(w.name, resolved)
+    traffic = measured_traffic(w.name, resolved) if args.op == "verify" else None
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "verify":
         print("[bench] timing the float64 oracle on a bounded sample (cpu_baseline)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, inp_cpu, args.cpu_budget)
 
@@ -172,6 +207,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V}",
+            "op": args.op,
             "N": w.N, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V,
             "in_dtype": w.dtype, "state_dtype": "f32", "gate": w.gate, "variant": resolved,
             "algorithmic_bytes_per_call": b_alg,

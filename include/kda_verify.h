@@ -136,6 +136,48 @@ kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_
                                   const float* state, void* o, float* inter_ssm, void* conv_window,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Pool indirection (PR#107 PR description: conv_state_indices, cache_indices and
+ * intermediate_state_indices, each normalised on its own). Each array is a device
+ * int32 array of N entries, or NULL for the identity (sequence n uses row n, and the
+ * pool then has N rows). Sequence n is a padding entry when any of its three indices is
+ * negative or not below the pool's row count: nothing is read or written for it (its
+ * rows of o are left as they were). Rows written by one call (conv_state and the two
+ * intermediate pools) must be distinct across the batch; the state pool is only read
+ * by a verify call and may be shared. */
+typedef struct {
+  const int32_t* conv_state_indices;         /* row of conv_state [conv_state_slots, C, 3] */
+  const int32_t* cache_indices;              /* row of state [state_slots, HV, K, V] */
+  const int32_t* intermediate_state_indices; /* row of inter_ssm [intermediate_slots, T, HV, K, V]
+                                                and conv_window [intermediate_slots, T, C, 3] */
+  int32_t conv_state_slots;
+  int32_t state_slots;
+  int32_t intermediate_slots;
+} kda_pool_desc;
+
+/* kda_conv_verify_decode on pooled buffers: conv_state, state, inter_ssm and conv_window
+ * are the pools described by *pools (row counts instead of N); mixed_qkv, gate, beta and o
+ * keep their per-call [N, ...] shapes. pools == NULL is the identity (the same as
+ * kda_conv_verify_decode). Same validation and error behaviour. */
+kda_status kda_conv_verify_decode_pooled(const kda_verify_params* p, const kda_pool_desc* pools,
+                                         const void* mixed_qkv, const void* conv_weight,
+                                         void* conv_state, const void* gate, const float* A_log,
+                                         const float* dt_bias, const void* beta, const float* state,
+                                         void* o, float* inter_ssm, void* conv_window,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* Accept step after a verify (PR#107 PR description: the per-token snapshots exist so the
+ * caller can roll back to the accepted prefix). accepted [N] (device int32) holds a_n,
+ * the number of tokens of sequence n that were kept, 1 <= a_n <= T. For each such n:
+ *   state[cache_indices[n]]           <- inter_ssm[intermediate_state_indices[n], a_n - 1]
+ *   conv_state[conv_state_indices[n]] <- conv_window[intermediate_state_indices[n], a_n - 1]
+ * Bit copies. Sequences with a_n outside [1, T], and padding entries, are left alone.
+ * p gives N, T, H, HV, K, V and in_dtype; pools as above (NULL = identity). */
+kda_status kda_verify_commit(const kda_verify_params* p, const kda_pool_desc* pools,
+                             const int32_t* accepted, const float* inter_ssm,
+                             const void* conv_window, float* state, void* conv_state,
+                             hipStream_t stream);
+
 /* Static text for a kda_status value (never NULL). */
 const char* kda_status_string(int32_t status);
 

@@ -45,6 +45,16 @@ class Params(ctypes.Structure):
     ]
 
 
+class PoolDesc(ctypes.Structure):
+    """Mirror of ``kda_pool_desc``."""
+
+    _fields_ = [
+        ("conv_state_indices", ctypes.c_void_p), ("cache_indices", ctypes.c_void_p),
+        ("intermediate_state_indices", ctypes.c_void_p), ("conv_state_slots", ctypes.c_int32),
+        ("state_slots", ctypes.c_int32), ("intermediate_slots", ctypes.c_int32),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -77,6 +87,11 @@ def load() -> ctypes.CDLL:
     lib.kda_validate.restype = ctypes.c_int
     lib.kda_conv_verify_decode.argtypes = [PP] + [_VP] * 12 + [_SZ, _VP]
     lib.kda_conv_verify_decode.restype = ctypes.c_int
+    PD = ctypes.POINTER(PoolDesc)
+    lib.kda_conv_verify_decode_pooled.argtypes = [PP, PD] + [_VP] * 12 + [_SZ, _VP]
+    lib.kda_conv_verify_decode_pooled.restype = ctypes.c_int
+    lib.kda_verify_commit.argtypes = [PP, PD] + [_VP] * 5 + [_VP]
+    lib.kda_verify_commit.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int32]
     lib.kda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -184,6 +199,79 @@ def kda_conv_verify_decode(p: Params, mixed_qkv, conv_weight, conv_state, gate, 
                                        workspace.numel() * workspace.element_size(), _VP(_stream(stream)))
     if st != KDA_OK:
         raise KdaError(st, "kda_conv_verify_decode")
+
+
+def _index(name, t, N):
+    if t is None:
+        return None
+    _check(name, t, (N,), torch.int32)
+    return t
+
+
+def make_pools(N: int, conv_state_indices=None, cache_indices=None, intermediate_state_indices=None,
+               conv_state_slots=None, state_slots=None, intermediate_slots=None) -> PoolDesc:
+    """A pool descriptor; each index array is an int32 [N] GPU tensor or None (identity)."""
+    for name, t in (("conv_state_indices", conv_state_indices), ("cache_indices", cache_indices),
+                    ("intermediate_state_indices", intermediate_state_indices)):
+        _index(name, t, N)
+    d = PoolDesc()
+    d.conv_state_indices = conv_state_indices.data_ptr() if conv_state_indices is not None else None
+    d.cache_indices = cache_indices.data_ptr() if cache_indices is not None else None
+    d.intermediate_state_indices = (intermediate_state_indices.data_ptr()
+                                    if intermediate_state_indices is not None else None)
+    d.conv_state_slots = N if conv_state_slots is None else conv_state_slots
+    d.state_slots = N if state_slots is None else state_slots
+    d.intermediate_slots = N if intermediate_slots is None else intermediate_slots
+    return d
+
+
+def kda_conv_verify_decode_pooled(p: Params, pools: PoolDesc, mixed_qkv, conv_weight, conv_state, gate, A_log,
+                                  dt_bias, beta, state, o, inter_ssm, conv_window, workspace, stream=None) -> None:
+    """The verify step on pooled conv_state / state / inter_ssm / conv_window (see kda_pool_desc)."""
+    N, T, H, HV, K, V = p.N, p.T, p.H, p.HV, p.K, p.V
+    C = 2 * H * K + HV * V
+    dt = _TORCH_DT.get(p.in_dtype)
+    if dt is None:
+        raise KdaError(-3, "kda_conv_verify_decode_pooled")
+    _check("mixed_qkv", mixed_qkv, (N, T, C), dt)
+    _check("conv_weight", conv_weight, (C, 4), dt)
+    _check("conv_state", conv_state, (pools.conv_state_slots, C, 3), dt)
+    _check("gate", gate, (N, T, HV, K), dt)
+    _check("A_log", A_log, (HV,), torch.float32)
+    _check("dt_bias", dt_bias, (HV * K,), torch.float32)
+    _check("beta", beta, (N, T, HV), dt)
+    _check("state", state, (pools.state_slots, HV, K, V), torch.float32)
+    _check("o", o, (N, T, HV, V), dt)
+    _check("inter_ssm", inter_ssm, (pools.intermediate_slots, T, HV, K, V), torch.float32)
+    _check("conv_window", conv_window, (pools.intermediate_slots, T, C, 3), dt)
+    ptrs = [t.data_ptr() for t in (mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
+                                   o, inter_ssm, conv_window, workspace)]
+    st = load().kda_conv_verify_decode_pooled(ctypes.byref(p), ctypes.byref(pools), *[_VP(x) for x in ptrs],
+                                              workspace.numel() * workspace.element_size(), _VP(_stream(stream)))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_conv_verify_decode_pooled")
+
+
+def verify_commit(p: Params, pools: PoolDesc, accepted, inter_ssm, conv_window, state, conv_state,
+                  stream=None) -> None:
+    """Accept step: state/conv_state rows <- the snapshots of each sequence's last accepted token."""
+    N, T, H, HV, K, V = p.N, p.T, p.H, p.HV, p.K, p.V
+    C = 2 * H * K + HV * V
+    dt = _TORCH_DT.get(p.in_dtype)
+    if dt is None:
+        raise KdaError(-3, "kda_verify_commit")
+    if pools is None:
+        pools = make_pools(N)
+    _check("accepted", accepted, (N,), torch.int32)
+    _check("inter_ssm", inter_ssm, (pools.intermediate_slots, T, HV, K, V), torch.float32)
+    _check("conv_window", conv_window, (pools.intermediate_slots, T, C, 3), dt)
+    _check("state", state, (pools.state_slots, HV, K, V), torch.float32)
+    _check("conv_state", conv_state, (pools.conv_state_slots, C, 3), dt)
+    ptrs = [t.data_ptr() for t in (accepted, inter_ssm, conv_window, state, conv_state)]
+    st = load().kda_verify_commit(ctypes.byref(p), ctypes.byref(pools), *[_VP(x) for x in ptrs],
+                                  _VP(_stream(stream)))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_verify_commit")
 
 
 def alloc_outputs(w, device="cuda") -> Dict[str, torch.Tensor]:

@@ -162,6 +162,11 @@ struct Args {
   float* inter_ssm;
   void* conv_window;
   uint32_t* counters;
+  // pool rows (NULL: the identity); a sequence with any index outside its pool is skipped
+  const int32_t* cs_idx;
+  const int32_t* st_idx;
+  const int32_t* in_idx;
+  int cs_slots, st_slots, in_slots;
   int N, T, H, HV, C;
   int g;      // HV / H
   int group;  // WGs reading one q/k head's conv cache: g * (V-tiles)
@@ -279,6 +284,13 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   const int unit = lb / CF::NVT;  // n * HV + hv
   const int hv = unit % HV, n = unit / HV;
   const int h = hv / a.g;
+  // pool rows of this sequence: conv cache, state, and the snapshot / window pools
+  const int cs_row = a.cs_idx ? a.cs_idx[n] : n;
+  const int st_row = a.st_idx ? a.st_idx[n] : n;
+  const int in_row = a.in_idx ? a.in_idx[n] : n;
+  if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
+      in_row >= a.in_slots)
+    return;  // padding entry: the whole WG (and its group) skips, nothing is read or written
 
   const R* __restrict__ xq = static_cast<const R*>(a.mixed_qkv);
   const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
@@ -312,7 +324,7 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
       dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
     } else if ((ci -= nA) < nB) {
       const int e = ci * E16, lc = e / 3;
-      src = cstate + ((size_t)n * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
+      src = cstate + ((size_t)cs_row * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
       dst = (int)((char*)&s.cs[e] - lds);
     } else if ((ci -= nB) < nC) {
       const int e = ci * E16, lc = e / 4;
@@ -337,7 +349,7 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   const int col = vt * VT + c4 * 4;
   const int row0 = wave * CF::RW + qq;  // this lane's rows: row0 + Q * r
   const size_t KV = (size_t)K * V;
-  const float* sp = a.state + (size_t)unit * KV + (size_t)row0 * V + col;
+  const float* sp = a.state + ((size_t)st_row * HV + hv) * KV + (size_t)row0 * V + col;
   f32x4 S[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r)
@@ -517,11 +529,12 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     d[2] = bt * (vv.z - uu.z);
     d[3] = bt * (vv.w - uu.w);
     const size_t nth = (size_t)(n * T + t) * HV + hv;
+    const size_t ith = ((size_t)in_row * T + t) * HV + hv;
     if (wave == 0 && qq == 0)
       OutVec<R>::store(a.o, nth * V + col, fmaf(qk, d[0], ww.x), fmaf(qk, d[1], ww.y),
                        fmaf(qk, d[2], ww.z), fmaf(qk, d[3], ww.w));
     // S_ij <- a_i S_ij + k_i d_j, then stream the snapshot out
-    float* dst = snap + nth * KV;
+    float* dst = snap + ith * KV;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       const f32x4 rr = rw[r * Q];
@@ -568,8 +581,8 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
         seg_lc = 2 * K;
       }
       const int gc0 = gchan<CF>(seg_lc, h, H, hv, vt);
-      R* dst = tok < 0 ? cstate + ((size_t)n * C + gc0) * 3
-                       : cw + ((size_t)(n * T + tok) * C + gc0) * 3;
+      R* dst = tok < 0 ? cstate + ((size_t)cs_row * C + gc0) * 3
+                       : cw + (((size_t)in_row * T + tok) * C + gc0) * 3;
       put_window_vec<CF, R>(s, dst, seg_lc, tok, T, m);
     }
   }
@@ -578,8 +591,60 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     for (int q = tid; q < 2 * VQK; q += NTHR) {
       const int seg = q / VQK, m = q - seg * VQK;
       const int gc0 = gchan<CF>(seg * K, h, H, hv, vt);
-      put_window_vec<CF, R>(s, cstate + ((size_t)n * C + gc0) * 3, seg * K, -1, T, m);
+      put_window_vec<CF, R>(s, cstate + ((size_t)cs_row * C + gc0) * 3, seg * K, -1, T, m);
     }
+  }
+}
+
+// Accept step: one WG per (sequence, value head) copies the state snapshot of the last
+// accepted token into the state pool; the hv == 0 WG of the sequence also copies that
+// token's raw conv window into the conv cache pool. Pure 16-byte copies.
+struct CommitArgs {
+  const int32_t* accepted;
+  const float* inter_ssm;
+  const void* conv_window;
+  float* state;
+  void* conv_state;
+  const int32_t* cs_idx;
+  const int32_t* st_idx;
+  const int32_t* in_idx;
+  int cs_slots, st_slots, in_slots;
+  int N, T, HV, C;
+  int kv4;     // K * V / 4 vectors per unit
+  int cs_vec;  // 16-byte vectors in one conv cache row (C * 3 elements)
+};
+
+__global__ __launch_bounds__(256) void kda_commit_kernel(const CommitArgs a) {
+  const int unit = xcd_order(blockIdx.x, gridDim.x), n = unit / a.HV, hv = unit % a.HV;
+  const int acc = a.accepted[n];
+  const int cs_row = a.cs_idx ? a.cs_idx[n] : n;
+  const int st_row = a.st_idx ? a.st_idx[n] : n;
+  const int in_row = a.in_idx ? a.in_idx[n] : n;
+  if (acc < 1 || acc > a.T || cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots ||
+      in_row < 0 || in_row >= a.in_slots)
+    return;
+  const size_t src_tok = (size_t)in_row * a.T + (acc - 1);
+  const f32x4* __restrict__ src = reinterpret_cast<const f32x4*>(a.inter_ssm) + (src_tok * a.HV + hv) * (size_t)a.kv4;
+  f32x4* __restrict__ dst = reinterpret_cast<f32x4*>(a.state) + ((size_t)st_row * a.HV + hv) * (size_t)a.kv4;
+  // chunks of 8 vectors per thread: all loads of a chunk are in flight before its stores
+  constexpr int U = 8;
+  for (int base = 0; base < a.kv4; base += U * 256) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * 256 + (int)threadIdx.x;
+      if (i < a.kv4) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * 256 + (int)threadIdx.x;
+      if (i < a.kv4) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
+  if (hv == 0) {
+    const u32x4* __restrict__ cw = reinterpret_cast<const u32x4*>(a.conv_window) + src_tok * (size_t)a.cs_vec;
+    u32x4* __restrict__ cs = reinterpret_cast<u32x4*>(a.conv_state) + (size_t)cs_row * a.cs_vec;
+    for (int i = threadIdx.x; i < a.cs_vec; i += blockDim.x) cs[i] = cw[i];
   }
 }
 
@@ -731,12 +796,63 @@ int32_t kda_select_variant(const kda_verify_params* p) {
   return units >= 4096 ? KDA_VARIANT_SMALL : KDA_VARIANT_LARGE;
 }
 
-kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
-                        const void* conv_state, const void* gate, const float* A_log, const float* dt_bias,
-                        const void* beta, const float* state, const void* o, const float* inter_ssm,
-                        const void* conv_window, const void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace kda {
+
+// Pool rows and index arrays of a call; the identity when pools == NULL.
+struct PoolView {
+  const int32_t* cs_idx = nullptr;
+  const int32_t* st_idx = nullptr;
+  const int32_t* in_idx = nullptr;
+  size_t cs_slots, st_slots, in_slots;
+};
+
+kda_status pool_view(const kda_verify_params* p, const kda_pool_desc* pools, PoolView* v) {
+  v->cs_slots = v->st_slots = v->in_slots = (size_t)p->N;
+  if (!pools) return KDA_OK;
+  if (pools->conv_state_slots < 1 || pools->state_slots < 1 || pools->intermediate_slots < 1) return KDA_ERR_SHAPE;
+  if ((long long)pools->state_slots * p->HV * 8 > 0x7fffffffLL) return KDA_ERR_SHAPE;
+  const int32_t* idx[] = {pools->conv_state_indices, pools->cache_indices, pools->intermediate_state_indices};
+  for (const int32_t* q : idx)
+    if (reinterpret_cast<uintptr_t>(q) & 3u) return KDA_ERR_ALIGN;
+  v->cs_idx = pools->conv_state_indices;
+  v->st_idx = pools->cache_indices;
+  v->in_idx = pools->intermediate_state_indices;
+  // a NULL index array is the identity, which needs at least N rows
+  v->cs_slots = pools->conv_state_slots;
+  v->st_slots = pools->state_slots;
+  v->in_slots = pools->intermediate_slots;
+  if ((!v->cs_idx && v->cs_slots < (size_t)p->N) || (!v->st_idx && v->st_slots < (size_t)p->N) ||
+      (!v->in_idx && v->in_slots < (size_t)p->N))
+    return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+Range rg(const void* q, size_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+  return Range{lo, lo + bytes};
+}
+
+// Written ranges must not overlap each other or any read range.
+bool any_alias(const Range* in, size_t nin, const Range* out, size_t nout) {
+  for (size_t i = 0; i < nout; ++i) {
+    for (size_t j = i + 1; j < nout; ++j)
+      if (overlap(out[i], out[j])) return true;
+    for (size_t j = 0; j < nin; ++j)
+      if (overlap(out[i], in[j])) return true;
+  }
+  return false;
+}
+
+kda_status validate_verify(const kda_verify_params* p, const kda_pool_desc* pools, PoolView* pv,
+                           const void* mixed_qkv, const void* conv_weight, const void* conv_state, const void* gate,
+                           const float* A_log, const float* dt_bias, const void* beta, const float* state,
+                           const void* o, const float* inter_ssm, const void* conv_window, const void* workspace,
+                           size_t workspace_bytes) {
   kda_status st = check_params(p);
   if (st != KDA_OK) return st;
+  if ((st = pool_view(p, pools, pv)) != KDA_OK) return st;
   if (p->N == 0) return KDA_OK;
   const void* ptrs[] = {mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias,
                         beta,      state,       o,          inter_ssm, conv_window, workspace};
@@ -749,31 +865,45 @@ kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const
   const size_t s = p->in_dtype == KDA_BF16 ? 2 : 4;
   const size_t N = p->N, T = p->T, HV = p->HV, K = p->K, V = p->V;
   const size_t C = 2 * (size_t)p->H * K + HV * V;
-  auto rg = [](const void* q, size_t bytes) {
-    uintptr_t lo = reinterpret_cast<uintptr_t>(q);
-    return Range{lo, lo + bytes};
-  };
-  const Range in[] = {rg(mixed_qkv, s * N * T * C), rg(conv_weight, s * C * 4), rg(gate, s * N * T * HV * K),
-                      rg(A_log, 4 * HV),            rg(dt_bias, 4 * HV * K),   rg(beta, s * N * T * HV),
-                      rg(state, 4 * N * HV * K * V)};
-  const Range out[] = {rg(conv_state, s * N * C * 3), rg(o, s * N * T * HV * V), rg(inter_ssm, 4 * N * T * HV * K * V),
-                       rg(conv_window, s * N * T * C * 3), rg(workspace, kda_workspace_bytes(p))};
-  // written buffers must not overlap each other or any read buffer
-  for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
-    for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
-      if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
-    for (const Range& r : in)
-      if (overlap(out[i], r)) return KDA_ERR_ALIAS;
-  }
+  const Range in[] = {rg(mixed_qkv, s * N * T * C),
+                      rg(conv_weight, s * C * 4),
+                      rg(gate, s * N * T * HV * K),
+                      rg(A_log, 4 * HV),
+                      rg(dt_bias, 4 * HV * K),
+                      rg(beta, s * N * T * HV),
+                      rg(state, 4 * pv->st_slots * HV * K * V),
+                      rg(pv->cs_idx, pv->cs_idx ? 4 * N : 0),
+                      rg(pv->st_idx, pv->st_idx ? 4 * N : 0),
+                      rg(pv->in_idx, pv->in_idx ? 4 * N : 0)};
+  const Range out[] = {rg(conv_state, s * pv->cs_slots * C * 3), rg(o, s * N * T * HV * V),
+                       rg(inter_ssm, 4 * pv->in_slots * T * HV * K * V), rg(conv_window, s * pv->in_slots * T * C * 3),
+                       rg(workspace, kda_workspace_bytes(p))};
+  if (any_alias(in, sizeof(in) / sizeof(in[0]), out, sizeof(out) / sizeof(out[0]))) return KDA_ERR_ALIAS;
   return KDA_OK;
 }
 
-kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
-                                  void* conv_state, const void* gate, const float* A_log, const float* dt_bias,
-                                  const void* beta, const float* state, void* o, float* inter_ssm,
-                                  void* conv_window, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  kda_status st = kda_validate(p, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o,
-                               inter_ssm, conv_window, workspace, workspace_bytes);
+}  // namespace kda
+
+extern "C" {
+
+kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
+                        const void* conv_state, const void* gate, const float* A_log, const float* dt_bias,
+                        const void* beta, const float* state, const void* o, const float* inter_ssm,
+                        const void* conv_window, const void* workspace, size_t workspace_bytes) {
+  PoolView pv;
+  return validate_verify(p, nullptr, &pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o,
+                         inter_ssm, conv_window, workspace, workspace_bytes);
+}
+
+kda_status kda_conv_verify_decode_pooled(const kda_verify_params* p, const kda_pool_desc* pools,
+                                         const void* mixed_qkv, const void* conv_weight, void* conv_state,
+                                         const void* gate, const float* A_log, const float* dt_bias,
+                                         const void* beta, const float* state, void* o, float* inter_ssm,
+                                         void* conv_window, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  PoolView pv;
+  kda_status st = validate_verify(p, pools, &pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta,
+                                  state, o, inter_ssm, conv_window, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
   if (p->N == 0) return KDA_OK;
   const Tile tl = choose_tile(p->K, p->V, kda_select_variant(p), p->N, p->T, p->HV);
@@ -793,6 +923,12 @@ kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_
   a.inter_ssm = inter_ssm;
   a.conv_window = conv_window;
   a.counters = static_cast<uint32_t*>(workspace);
+  a.cs_idx = pv.cs_idx;
+  a.st_idx = pv.st_idx;
+  a.in_idx = pv.in_idx;
+  a.cs_slots = (int)pv.cs_slots;
+  a.st_slots = (int)pv.st_slots;
+  a.in_slots = (int)pv.in_slots;
   a.N = p->N;
   a.T = p->T;
   a.H = p->H;
@@ -807,6 +943,63 @@ kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->K);
   a.eps = p->l2norm_eps;
   return fn(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
+                                  void* conv_state, const void* gate, const float* A_log, const float* dt_bias,
+                                  const void* beta, const float* state, void* o, float* inter_ssm,
+                                  void* conv_window, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kda_conv_verify_decode_pooled(p, nullptr, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta,
+                                       state, o, inter_ssm, conv_window, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_verify_commit(const kda_verify_params* p, const kda_pool_desc* pools, const int32_t* accepted,
+                             const float* inter_ssm, const void* conv_window, float* state, void* conv_state,
+                             hipStream_t stream) {
+  kda_status st = check_params(p);
+  if (st != KDA_OK) return st;
+  PoolView pv;
+  if ((st = pool_view(p, pools, &pv)) != KDA_OK) return st;
+  if (p->N == 0) return KDA_OK;
+  const void* ptrs[] = {accepted, inter_ssm, conv_window, state, conv_state};
+  for (const void* q : ptrs)
+    if (!q) return KDA_ERR_NULL;
+  for (const void* q : ptrs)
+    if (misaligned(q)) return KDA_ERR_ALIGN;
+  const size_t s = p->in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t N = p->N, T = p->T, HV = p->HV, K = p->K, V = p->V;
+  const size_t C = 2 * (size_t)p->H * K + HV * V;
+  const Range in[] = {rg(accepted, 4 * N),
+                      rg(inter_ssm, 4 * pv.in_slots * T * HV * K * V),
+                      rg(conv_window, s * pv.in_slots * T * C * 3),
+                      rg(pv.cs_idx, pv.cs_idx ? 4 * N : 0),
+                      rg(pv.st_idx, pv.st_idx ? 4 * N : 0),
+                      rg(pv.in_idx, pv.in_idx ? 4 * N : 0)};
+  const Range out[] = {rg(state, 4 * pv.st_slots * HV * K * V), rg(conv_state, s * pv.cs_slots * C * 3)};
+  if (any_alias(in, sizeof(in) / sizeof(in[0]), out, sizeof(out) / sizeof(out[0]))) return KDA_ERR_ALIAS;
+  CommitArgs a;
+  a.accepted = accepted;
+  a.inter_ssm = inter_ssm;
+  a.conv_window = conv_window;
+  a.state = state;
+  a.conv_state = conv_state;
+  a.cs_idx = pv.cs_idx;
+  a.st_idx = pv.st_idx;
+  a.in_idx = pv.in_idx;
+  a.cs_slots = (int)pv.cs_slots;
+  a.st_slots = (int)pv.st_slots;
+  a.in_slots = (int)pv.in_slots;
+  a.N = p->N;
+  a.T = p->T;
+  a.HV = p->HV;
+  a.C = (int)C;
+  a.kv4 = (int)(K * V / 4);
+  a.cs_vec = (int)(C * 3 * s / 16);
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_commit_kernel), dim3((unsigned)(N * HV)), dim3(256),
+                         args, 0, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
 }
 
 kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream) {

@@ -184,3 +184,73 @@ def verify_workload(w, inputs: Dict, **kw) -> Dict[str, np.ndarray]:
     """``verify`` with the shape and gate form taken from a ``synth.Workload``."""
     return verify(inputs, H=w.H, HV=w.HV, K=w.K, V=w.V,
                   gate_mode=GATE_SAFE if w.gate == "safe" else GATE_SOFTPLUS, **kw)
+
+
+def verify_pooled(inputs: Dict, pools: Dict, *, H: int, HV: int, K: int, V: int, gate_mode: int,
+                  **kw) -> Dict[str, np.ndarray]:
+    """The verify step on pooled buffers (PR#107 PR description: conv_state_indices,
+    cache_indices and intermediate_state_indices, each normalised on its own).
+
+    ``inputs`` holds the per-call tensors (mixed_qkv, conv_weight, gate, A_log, dt_bias,
+    beta) and the pools ``conv_state`` [Pc,C,3] and ``state`` [Ps,HV,K,V]; ``pools`` holds
+    the index arrays (None = identity) and the initial contents of the written pools
+    ``inter_ssm`` [Pi,T,HV,K,V], ``conv_window`` [Pi,T,C,3] and of ``o`` [N,T,HV,V].
+    Sequence n is padding (skipped) when any of its indices is outside its pool. Each
+    sequence is gathered, run through ``verify`` and scattered back. Returns float64
+    copies of o, inter_ssm, conv_window and conv_state after the call.
+    """
+    x = f64(inputs["mixed_qkv"])
+    N = x.shape[0]
+    cs_pool = f64(inputs["conv_state"]).copy()
+    st_pool = f64(inputs["state"])
+    out_o = f64(pools["o"]).copy()
+    out_is = f64(pools["inter_ssm"]).copy()
+    out_cw = f64(pools["conv_window"]).copy()
+
+    def rows(key, slots):
+        idx = pools.get(key)
+        return np.arange(N) if idx is None else np.asarray(f64(idx), dtype=np.int64)
+
+    cs_i = rows("conv_state_indices", cs_pool.shape[0])
+    st_i = rows("cache_indices", st_pool.shape[0])
+    in_i = rows("intermediate_state_indices", out_is.shape[0])
+    for n in range(N):
+        c, s_, i = cs_i[n], st_i[n], in_i[n]
+        if not (0 <= c < cs_pool.shape[0] and 0 <= s_ < st_pool.shape[0] and 0 <= i < out_is.shape[0]):
+            continue
+        one = {
+            "mixed_qkv": x[n:n + 1], "conv_weight": inputs["conv_weight"],
+            "conv_state": cs_pool[c:c + 1], "gate": f64(inputs["gate"])[n:n + 1],
+            "A_log": inputs["A_log"], "dt_bias": inputs["dt_bias"],
+            "beta": f64(inputs["beta"])[n:n + 1], "state": st_pool[s_:s_ + 1],
+        }
+        r = verify(one, H=H, HV=HV, K=K, V=V, gate_mode=gate_mode, **kw)
+        out_o[n] = r["o"][0]
+        out_is[i] = r["inter_ssm"][0]
+        out_cw[i] = r["conv_window"][0]
+        cs_pool[c] = r["conv_state"][0]
+    return {"o": out_o, "inter_ssm": out_is, "conv_window": out_cw, "conv_state": cs_pool}
+
+
+def commit(accepted, pools: Dict, inter_ssm, conv_window, state, conv_state, T: int) -> Dict[str, np.ndarray]:
+    """Accept step: for each sequence n with 1 <= a_n <= T (and valid indices),
+    state[cache_indices[n]] <- inter_ssm[intermediate_state_indices[n], a_n - 1] and
+    conv_state[conv_state_indices[n]] <- conv_window[intermediate_state_indices[n], a_n - 1].
+    Returns float64 copies of the state and conv_state pools."""
+    acc = np.asarray(f64(accepted), dtype=np.int64)
+    N = acc.shape[0]
+    isp, cwp = f64(inter_ssm), f64(conv_window)
+    st, cs = f64(state).copy(), f64(conv_state).copy()
+
+    def rows(key):
+        idx = pools.get(key) if pools else None
+        return np.arange(N) if idx is None else np.asarray(f64(idx), dtype=np.int64)
+
+    cs_i, st_i, in_i = rows("conv_state_indices"), rows("cache_indices"), rows("intermediate_state_indices")
+    for n in range(N):
+        a, c, s_, i = acc[n], cs_i[n], st_i[n], in_i[n]
+        if not (1 <= a <= T and 0 <= c < cs.shape[0] and 0 <= s_ < st.shape[0] and 0 <= i < isp.shape[0]):
+            continue
+        st[s_] = isp[i, a - 1]
+        cs[c] = cwp[i, a - 1]
+    return {"state": st, "conv_state": cs}

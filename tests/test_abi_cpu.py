@@ -157,3 +157,41 @@ def test_oracle_and_gpu_path_share_no_code():
         if f.endswith((".py", ".c", ".h")):
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "linear_attention_decode_kda_amd" not in text and "kda_verify" not in text, f
+
+
+def _pooled_raw(lib, p, pd, ptrs, wsb):
+    return lib.kda_conv_verify_decode_pooled(ctypes.byref(p), ctypes.byref(pd) if pd is not None else None,
+                                             *[ctypes.c_void_p(x) for x in ptrs], wsb, None)
+
+
+def test_pool_descriptor_validation(lib):
+    """Pool errors are caught on the host before any launch (fake pointers, no GPU)."""
+    p = kda.make_params(4, 4, 2, 4, 128, 128)
+    p.T = 0  # invalid params first: nothing reaches the pools
+    ptrs, wsb = _fake_ptrs(kda.make_params(4, 4, 2, 4, 128, 128))
+    assert _pooled_raw(lib, p, kda.PoolDesc(), ptrs, wsb) == -2
+    p = kda.make_params(4, 4, 2, 4, 128, 128)
+    pd = kda.PoolDesc()
+    pd.conv_state_slots, pd.state_slots, pd.intermediate_slots = 4, 0, 4
+    assert _pooled_raw(lib, p, pd, ptrs, wsb) == -2  # an empty pool
+    pd.state_slots = 3
+    assert _pooled_raw(lib, p, pd, ptrs, wsb) == -2  # identity rows need N slots
+    pd.state_slots = 3
+    pd.cache_indices = (13 << 40) + 2
+    assert _pooled_raw(lib, p, pd, ptrs, wsb) == -4  # misaligned index array
+    pd.cache_indices = ptrs[9]
+    assert _pooled_raw(lib, p, pd, ptrs, wsb) == -7  # index array inside inter_ssm (written)
+
+
+def test_commit_validation(lib):
+    p = kda.make_params(4, 4, 2, 4, 128, 128)
+    ptrs = [(i + 1) << 40 for i in range(5)]
+    args = lambda q: [ctypes.c_void_p(x) for x in q]  # noqa: E731
+    bad = list(ptrs)
+    bad[0] = 0
+    assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -1
+    bad = list(ptrs)
+    bad[3] = ptrs[1]  # state written over inter_ssm
+    assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -7
+    p0 = kda.make_params(0, 4, 2, 4, 128, 128)
+    assert lib.kda_verify_commit(ctypes.byref(p0), None, *args([0] * 5), None) == 0

@@ -1,0 +1,225 @@
+"""GPU parity of the pooled verify step and the accept (commit) step.
+
+Page: "[KDA] Fuse causal conv1d into MTP verify decode #107" (cuLA pull request),
+PR description: conv_state_indices, cache_indices and intermediate_state_indices,
+normalised independently; per-token snapshots for rolling back to the accepted prefix.
+Tests & Accuracy: independent, non-contiguous state indices; repeated verify chains.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_decode_kda_amd as kda
+import oracle
+from linear_attention_decode_kda_amd import synth
+from gpu_util import TOL, bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def W(N, T, H, HV, K=128, V=128, dtype="bf16", gate="softplus", seed=9):
+    return synth.Workload(f"pool{N}x{T}x{H}x{HV}x{K}", N=N, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype, gate=gate,
+                          seed=seed)
+
+
+def _gm(w):
+    return oracle.GATE_SAFE if w.gate == "safe" else oracle.GATE_SOFTPLUS
+
+
+def _pooled_case(w, slots, seed, pad=()):
+    """Pools larger than N, rows picked at random without repeats; ``pad`` sequences get -1."""
+    inp = synth.make_inputs(w)
+    g = torch.Generator().manual_seed(seed)
+    Pc, Ps, Pi = slots
+    cs_idx = torch.randperm(Pc, generator=g)[: w.N].to(torch.int32)
+    st_idx = torch.randperm(Ps, generator=g)[: w.N].to(torch.int32)
+    in_idx = torch.randperm(Pi, generator=g)[: w.N].to(torch.int32)
+    for n in pad:
+        st_idx[n] = -1
+    dt = w.torch_dtype
+    cs_pool = torch.randn(Pc, w.C, 3, generator=g).to(dt)
+    st_pool = torch.randn(Ps, w.HV, w.K, w.V, generator=g) * 0.1
+    cs_pool[cs_idx.long()] = inp["conv_state"]
+    keep = st_idx >= 0
+    st_pool[st_idx[keep].long()] = inp["state"][keep]
+    o0 = torch.randn(w.N, w.T, w.HV, w.V, generator=g).to(dt)
+    is0 = torch.randn(Pi, w.T, w.HV, w.K, w.V, generator=g)
+    cw0 = torch.randn(Pi, w.T, w.C, 3, generator=g).to(dt)
+    pinp = dict(inp)
+    pinp["conv_state"], pinp["state"] = cs_pool, st_pool
+    idx = {"conv_state_indices": cs_idx, "cache_indices": st_idx, "intermediate_state_indices": in_idx}
+    init = {"o": o0, "inter_ssm": is0, "conv_window": cw0}
+    return pinp, idx, init
+
+
+def _run_pooled(w, pinp, idx, init, variant=kda.VARIANT_AUTO):
+    say(f"[gpu] pooled {w.name} {w.dtype} {w.gate} variant={variant}")
+    p = kda.params_for(w, variant=variant)
+    d = {k: v.cuda() for k, v in pinp.items()}
+    di = {k: v.cuda() for k, v in idx.items()}
+    out = {k: v.cuda() for k, v in init.items()}
+    pools = kda.make_pools(w.N, di["conv_state_indices"], di["cache_indices"], di["intermediate_state_indices"],
+                           d["conv_state"].shape[0], d["state"].shape[0], out["inter_ssm"].shape[0])
+    ws = kda.alloc_workspace(p)
+    kda.kda_conv_verify_decode_pooled(p, pools, d["mixed_qkv"], d["conv_weight"], d["conv_state"], d["gate"],
+                                      d["A_log"], d["dt_bias"], d["beta"], d["state"], out["o"],
+                                      out["inter_ssm"], out["conv_window"], ws)
+    torch.cuda.synchronize()
+    out["conv_state"] = d["conv_state"]
+    return out, d, di, pools, p
+
+
+def _compare(w, got, ref):
+    dt = w.torch_dtype
+    assert np.array_equal(bits(got["conv_window"]), bits(torch.from_numpy(ref["conv_window"]).to(dt)))
+    assert np.array_equal(bits(got["conv_state"]), bits(torch.from_numpy(ref["conv_state"]).to(dt)))
+    eo = np.abs(got["o"].float().cpu().numpy() - ref["o"]).max()
+    es = np.abs(got["inter_ssm"].cpu().numpy() - ref["inter_ssm"]).max()
+    assert eo <= TOL and es <= TOL, (eo, es)
+
+
+CASES = [
+    (W(5, 4, 2, 4), (9, 7, 11), (), kda.VARIANT_SMALL),
+    (W(5, 4, 2, 4, gate="safe"), (9, 7, 11), (1, 3), kda.VARIANT_LARGE),
+    (W(3, 2, 1, 2, K=16, V=16, dtype="f32"), (4, 5, 6), (0,), kda.VARIANT_AUTO),
+    (W(4, 8, 2, 2, K=64, V=64), (8, 4, 5), (2,), kda.VARIANT_AUTO),
+]
+
+
+@pytest.mark.parametrize("w,slots,pad,variant", CASES, ids=[f"{c[0].name}-pad{len(c[2])}-v{c[3]}" for c in CASES])
+def test_pooled_verify_matches_oracle(w, slots, pad, variant):
+    pinp, idx, init = _pooled_case(w, slots, seed=5, pad=pad)
+    got, *_ = _run_pooled(w, pinp, idx, init, variant)
+    ref = oracle.verify_pooled(pinp, {**idx, **init}, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    _compare(w, got, ref)
+
+
+def test_pooled_identity_equals_dense_call():
+    w = W(6, 3, 2, 4)
+    inp = synth.make_inputs(w)
+    p = kda.params_for(w)
+    a = {k: v.cuda() for k, v in inp.items()}
+    b = {k: v.cuda() for k, v in inp.items()}
+    oa, ob = kda.alloc_outputs(w), kda.alloc_outputs(w)
+    kda.run(p, a, oa, kda.alloc_workspace(p))
+    pools = kda.make_pools(w.N)
+    kda.kda_conv_verify_decode_pooled(p, pools, b["mixed_qkv"], b["conv_weight"], b["conv_state"], b["gate"],
+                                      b["A_log"], b["dt_bias"], b["beta"], b["state"], ob["o"], ob["inter_ssm"],
+                                      ob["conv_window"], kda.alloc_workspace(p))
+    torch.cuda.synchronize()
+    for k in oa:
+        assert torch.equal(oa[k], ob[k]), k
+    assert torch.equal(a["conv_state"], b["conv_state"])
+
+
+@pytest.mark.parametrize("w", [W(5, 4, 2, 4, gate="safe"), W(3, 3, 1, 1, K=16, V=16, dtype="f32")])
+def test_commit_matches_oracle_and_prefix_verify(w):
+    """Commit is a bit copy (exact against the oracle), and accepting a tokens gives the
+    state and conv cache a fresh verify of just those a tokens produces on the GPU."""
+    slots = (w.N + 3, w.N + 2, w.N + 4)
+    pinp, idx, init = _pooled_case(w, slots, seed=7)
+    out, d, di, pools, p = _run_pooled(w, pinp, idx, init)
+    acc = torch.tensor([(n % w.T) + 1 for n in range(w.N)], dtype=torch.int32)
+    acc[0] = 0  # nothing accepted
+    state_before = d["state"].clone()
+    cs_after_verify = d["conv_state"].clone()
+    kda.verify_commit(p, pools, acc.cuda(), out["inter_ssm"], out["conv_window"], d["state"], d["conv_state"])
+    torch.cuda.synchronize()
+    ref = oracle.commit(acc, idx, out["inter_ssm"], out["conv_window"], state_before, cs_after_verify, T=w.T)
+    assert torch.equal(d["state"].cpu(), torch.from_numpy(ref["state"]).float())
+    assert np.array_equal(bits(d["conv_state"]), bits(torch.from_numpy(ref["conv_state"]).to(w.torch_dtype)))
+    # accepted prefix: a dense verify of the first a tokens from the original inputs
+    inp = synth.make_inputs(w)
+    for n in range(1, w.N):
+        a = int(acc[n])
+        wa = w.with_(N=1, T=a)
+        one = {k: (v[n:n + 1, :a].contiguous() if k in ("mixed_qkv", "gate", "beta") else
+                   v[n:n + 1].contiguous() if k in ("conv_state", "state") else v).cuda()
+               for k, v in inp.items()}
+        po = kda.alloc_outputs(wa)
+        pp = kda.params_for(wa)
+        kda.run(pp, one, po, kda.alloc_workspace(pp))
+        torch.cuda.synchronize()
+        assert torch.equal(d["state"][idx["cache_indices"][n].item()], po["inter_ssm"][0, a - 1]), n
+        assert torch.equal(d["conv_state"][idx["conv_state_indices"][n].item()], one["conv_state"][0]), n
+
+
+def test_serving_loop_verify_commit_chain():
+    """Three rounds of verify -> commit on shared pools; each round's outputs match the
+    oracle run on the pools the previous rounds left."""
+    w = W(4, 4, 2, 4, gate="safe")
+    slots = (6, 6, 5)
+    pinp, idx, init = _pooled_case(w, slots, seed=11)
+    ref_cs, ref_st = oracle.f64(pinp["conv_state"]), oracle.f64(pinp["state"])
+    d = {k: v.cuda() for k, v in pinp.items()}
+    di = {k: v.cuda() for k, v in idx.items()}
+    out = {k: v.cuda() for k, v in init.items()}
+    p = kda.params_for(w)
+    pools = kda.make_pools(w.N, di["conv_state_indices"], di["cache_indices"], di["intermediate_state_indices"],
+                           *slots)
+    ws = kda.alloc_workspace(p)
+    for rnd in range(3):
+        fresh = synth.make_inputs(w, seed=100 + rnd)
+        for k in ("mixed_qkv", "gate", "beta"):
+            d[k].copy_(fresh[k])
+        before = {k: v.cpu() for k, v in out.items()}
+        kda.kda_conv_verify_decode_pooled(p, pools, d["mixed_qkv"], d["conv_weight"], d["conv_state"], d["gate"],
+                                          d["A_log"], d["dt_bias"], d["beta"], d["state"], out["o"],
+                                          out["inter_ssm"], out["conv_window"], ws)
+        acc = torch.tensor([1 + (n + rnd) % w.T for n in range(w.N)], dtype=torch.int32)
+        kda.verify_commit(p, pools, acc.cuda(), out["inter_ssm"], out["conv_window"], d["state"], d["conv_state"])
+        torch.cuda.synchronize()
+        rin = {"mixed_qkv": fresh["mixed_qkv"], "conv_weight": pinp["conv_weight"], "gate": fresh["gate"],
+               "A_log": pinp["A_log"], "dt_bias": pinp["dt_bias"], "beta": fresh["beta"],
+               "conv_state": ref_cs, "state": ref_st}
+        r = oracle.verify_pooled(rin, {**idx, **before}, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+        eo = np.abs(out["o"].float().cpu().numpy() - r["o"]).max()
+        es = np.abs(out["inter_ssm"].cpu().numpy() - r["inter_ssm"]).max()
+        assert eo <= TOL and es <= TOL, (rnd, eo, es)
+        c = oracle.commit(acc, idx, r["inter_ssm"], r["conv_window"], ref_st, r["conv_state"], T=w.T)
+        ref_cs, ref_st = c["conv_state"], c["state"]
+        assert np.array_equal(bits(d["conv_state"]), bits(torch.from_numpy(ref_cs).to(w.torch_dtype))), rnd
+        assert np.abs(d["state"].cpu().numpy() - ref_st).max() <= TOL, rnd
+
+
+def test_pool_argument_errors():
+    w = W(3, 2, 1, 2)
+    p = kda.params_for(w)
+    inp = {k: v.cuda() for k, v in synth.make_inputs(w).items()}
+    out = kda.alloc_outputs(w)
+    ws = kda.alloc_workspace(p)
+
+    def call(pools):
+        kda.kda_conv_verify_decode_pooled(p, pools, inp["mixed_qkv"], inp["conv_weight"], inp["conv_state"],
+                                          inp["gate"], inp["A_log"], inp["dt_bias"], inp["beta"], inp["state"],
+                                          out["o"], out["inter_ssm"], out["conv_window"], ws)
+
+    bad = kda.make_pools(w.N)
+    bad.state_slots = 0
+    with pytest.raises(Exception):
+        call(bad)
+    lib = kda.load()
+    import ctypes
+
+    ptrs = [t.data_ptr() for t in (inp["mixed_qkv"], inp["conv_weight"], inp["conv_state"], inp["gate"],
+                                   inp["A_log"], inp["dt_bias"], inp["beta"], inp["state"], out["o"],
+                                   out["inter_ssm"], out["conv_window"], ws)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def raw(pd):
+        return lib.kda_conv_verify_decode_pooled(ctypes.byref(p), ctypes.byref(pd), *[ctypes.c_void_p(x) for x in ptrs],
+                                                 ws.numel(), stream)
+
+    pd = kda.make_pools(w.N)
+    pd.state_slots = 0
+    assert raw(pd) == -2
+    pd = kda.make_pools(w.N)
+    pd.intermediate_slots = w.N - 1  # identity rows need N slots
+    assert raw(pd) == -2
+    idx = torch.zeros(w.N + 1, dtype=torch.int32, device="cuda")
+    pd = kda.make_pools(w.N)
+    pd.cache_indices = idx.data_ptr() + 2  # misaligned int32 array
+    assert raw(pd) == -4
+    pd = kda.make_pools(w.N)
+    pd.conv_state_indices = out["o"].data_ptr()  # index array inside a written buffer
+    assert raw(pd) == -7

@@ -410,3 +410,91 @@ def test_tiny_regression_fixture():
     np.testing.assert_allclose(out["inter_ssm"].sum(axis=(2, 3, 4)).reshape(-1), doc["inter_ssm_sum_by_nt"], rtol=1e-12)
     np.testing.assert_allclose(out["inter_ssm"][:, :, :, 0, :].reshape(-1), doc["inter_ssm_first_row"], rtol=1e-12, atol=1e-14)
     np.testing.assert_array_equal(out["conv_state"].reshape(-1), doc["conv_state"])
+
+
+# ---------------------------------------------------------------- pooled verify and commit
+def _pool_case(seed=41, N=4, T=3, H=2, HV=4, K=8, V=8, slots=(7, 6, 9), gate="safe"):
+    w, inp = _small_inputs(N=N, T=T, H=H, HV=HV, K=K, V=V, seed=seed, gate=gate)
+    r = np.random.default_rng(seed)
+    Pc, Ps, Pi = slots
+    cs_idx = r.permutation(Pc)[:N]
+    st_idx = r.permutation(Ps)[:N]
+    in_idx = r.permutation(Pi)[:N]
+    cs_pool = r.normal(size=(Pc, w.C, 3))
+    st_pool = r.normal(size=(Ps, HV, K, V)) * 0.1
+    cs_pool[cs_idx] = oracle.f64(inp["conv_state"])
+    st_pool[st_idx] = oracle.f64(inp["state"])
+    pools = {
+        "conv_state_indices": cs_idx, "cache_indices": st_idx, "intermediate_state_indices": in_idx,
+        "o": r.normal(size=(N, T, HV, V)), "inter_ssm": r.normal(size=(Pi, T, HV, K, V)),
+        "conv_window": r.normal(size=(Pi, T, w.C, 3)),
+    }
+    pinp = dict(inp)
+    pinp["conv_state"], pinp["state"] = cs_pool, st_pool
+    return w, inp, pinp, pools
+
+
+def _gm(w):
+    return oracle.GATE_SAFE if w.gate == "safe" else oracle.GATE_SOFTPLUS
+
+
+def test_pooled_identity_equals_dense():
+    w, inp = _small_inputs(N=3, T=4, H=1, HV=2)
+    dense = oracle.verify_workload(w, inp)
+    pools = {"o": np.zeros((w.N, w.T, w.HV, w.V)), "inter_ssm": np.zeros((w.N, w.T, w.HV, w.K, w.V)),
+             "conv_window": np.zeros((w.N, w.T, w.C, 3))}
+    got = oracle.verify_pooled(inp, pools, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    for k in dense:
+        np.testing.assert_array_equal(got[k], dense[k])
+
+
+def test_pooled_rows_scatter_and_untouched_rows_keep():
+    """Per-sequence results land in the rows the index arrays name; other rows keep their contents."""
+    w, inp, pinp, pools = _pool_case()
+    dense = oracle.verify_workload(w, inp)
+    got = oracle.verify_pooled(pinp, pools, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    cs_i, in_i = pools["conv_state_indices"], pools["intermediate_state_indices"]
+    np.testing.assert_array_equal(got["o"], dense["o"])
+    np.testing.assert_array_equal(got["inter_ssm"][in_i], dense["inter_ssm"])
+    np.testing.assert_array_equal(got["conv_window"][in_i], dense["conv_window"])
+    np.testing.assert_array_equal(got["conv_state"][cs_i], dense["conv_state"])
+    other_i = np.setdiff1d(np.arange(pools["inter_ssm"].shape[0]), in_i)
+    np.testing.assert_array_equal(got["inter_ssm"][other_i], pools["inter_ssm"][other_i])
+    other_c = np.setdiff1d(np.arange(pinp["conv_state"].shape[0]), cs_i)
+    np.testing.assert_array_equal(got["conv_state"][other_c], pinp["conv_state"][other_c])
+
+
+def test_pooled_padding_entries_are_skipped():
+    w, inp, pinp, pools = _pool_case(seed=43)
+    pools["cache_indices"] = pools["cache_indices"].copy()
+    pools["cache_indices"][1] = -1
+    pools["intermediate_state_indices"] = pools["intermediate_state_indices"].copy()
+    pools["intermediate_state_indices"][2] = pools["inter_ssm"].shape[0]  # one past the end
+    got = oracle.verify_pooled(pinp, pools, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    for n in (1, 2):
+        np.testing.assert_array_equal(got["o"][n], pools["o"][n])
+        c = pools["conv_state_indices"][n]
+        np.testing.assert_array_equal(got["conv_state"][c], pinp["conv_state"][c])
+    np.testing.assert_array_equal(got["inter_ssm"][pools["intermediate_state_indices"][1]],
+                                  pools["inter_ssm"][pools["intermediate_state_indices"][1]])
+
+
+@pytest.mark.parametrize("a", [1, 2, 3])
+def test_commit_equals_verify_of_the_accepted_prefix(a):
+    """Accepting a of T tokens leaves the state and conv cache a dense verify of just those
+    a tokens produces (an independent run of the step on the shorter input)."""
+    w, inp, pinp, pools = _pool_case(seed=47)
+    got = oracle.verify_pooled(pinp, pools, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    acc = np.full(w.N, a)
+    acc[0] = 0  # nothing accepted: left alone
+    c = oracle.commit(acc, pools, got["inter_ssm"], got["conv_window"], pinp["state"], got["conv_state"], T=w.T)
+    wa = w.with_(T=a)
+    pre = dict(inp)
+    pre["mixed_qkv"], pre["gate"], pre["beta"] = inp["mixed_qkv"][:, :a], inp["gate"][:, :a], inp["beta"][:, :a]
+    ref = oracle.verify_workload(wa, pre)
+    cs_i, st_i = pools["conv_state_indices"], pools["cache_indices"]
+    for n in range(1, w.N):
+        np.testing.assert_array_equal(c["state"][st_i[n]], ref["inter_ssm"][n, a - 1])
+        np.testing.assert_array_equal(c["conv_state"][cs_i[n]], ref["conv_state"][n])
+    np.testing.assert_array_equal(c["state"][st_i[0]], pinp["state"][st_i[0]])
+    np.testing.assert_array_equal(c["conv_state"][cs_i[0]], got["conv_state"][cs_i[0]])
