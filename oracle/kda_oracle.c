@@ -31,7 +31,7 @@
 #define ORACLE_W 4 /* conv width; the cache holds W-1 = 3 raw tokens */
 
 /* Extended raw sequence of one channel (PR#107 description: conv_state holds the
- * latest three raw inputs, the T new tokens follow them):
+ * three most recent raw inputs, then the T new tokens):
  *   e[tau] = conv_state[n,c,tau] for tau < 3, mixed_qkv[n,tau-3,c] otherwise. */
 static double ext_raw(const double* mixed_qkv, const double* conv_state, int T, int C,
                       int n, int c, int tau) {
@@ -64,7 +64,7 @@ void oracle_conv_silu(int N, int T, int C, const double* mixed_qkv, const double
 
 /* Rollback snapshots of the raw conv window and the rolled conv cache (PR#107
  * description: per-token convolution-window snapshots; conv_state rolled to the
- * latest three raw tokens). These are copies of raw inputs, no arithmetic:
+ * three most recent raw tokens). These are copies of raw inputs, no arithmetic:
  *   conv_window[n,t,c,j] = e[t+1+j]   (the cache to restore if tokens 0..t are kept)
  *   conv_state_out[n,c,j] = e[T+j]. */
 void oracle_conv_roll(int N, int T, int C, const double* mixed_qkv, const double* conv_state,

@@ -34,7 +34,7 @@ def _ext_seq(x, s):
 # ---------------------------------------------------------------- conv window / conv_state
 @pytest.mark.parametrize("T", [1, 2, 3, 5])
 def test_conv_roll_is_shift_register(T):
-    """PR#107 description: conv_state keeps the latest three raw tokens; the per-token
+    """PR#107 description: conv_state holds the three most recent raw tokens; the per-token
     window is the cache that a rollback to token t restores. Values encode (n, tau, c),
     so any misplaced element is seen."""
     N, C = 3, 7
