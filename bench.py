@@ -77,17 +77,93 @@ def cpu_baseline(w, inp_cpu, budget_s: float):
     }
 
 
+def sweep(out_path: str, quick: bool = False) -> None:
+    """H = HV x T x N sweep over every tile width and snapshot store policy (K = V = 128,
+    bf16, softplus). Buffer sets are rotated so that at least 1 GiB is touched between
+    reuses (small shapes would otherwise run from the 256 MB last-level cache). Writes one
+    JSON object per shape to out_path and prints a summary table."""
+    import torch
+
+    import linear_attention_decode_kda_amd as kda
+    from linear_attention_decode_kda_amd import synth
+
+    dev = torch.device("cuda:0")
+    Hs = (8, 32) if quick else (8, 16, 32, 64)
+    Ts = (2, 4, 8) if quick else (1, 2, 4, 6, 8)
+    Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+    combos = [(t, pol) for t in (32, 64, 128) for pol in (1, 2)]
+    rows = []
+    with open(out_path, "w") as f:
+        for H in Hs:
+            for T in Ts:
+                for N in Ns:
+                    w = synth.Workload(f"sweep", N=N, T=T, H=H, HV=H, K=128, V=128, dtype="bf16",
+                                       gate="softplus", seed=1)
+                    b_alg = synth.algorithmic_bytes(w)
+                    nset = max(1, min(16, (1 << 30) // b_alg + 1))
+                    sets = []
+                    for _ in range(nset):
+                        inp = {
+                            "mixed_qkv": torch.randn(N, T, w.C, device=dev).to(torch.bfloat16),
+                            "conv_weight": (torch.randn(w.C, 4, device=dev) * 0.5).to(torch.bfloat16),
+                            "conv_state": torch.randn(N, w.C, 3, device=dev).to(torch.bfloat16),
+                            "gate": torch.randn(N, T, H, 128, device=dev).to(torch.bfloat16),
+                            "A_log": torch.rand(H, device=dev),
+                            "dt_bias": torch.randn(H * 128, device=dev) * 0.1,
+                            "beta": torch.randn(N, T, H, device=dev).to(torch.bfloat16),
+                            "state": torch.randn(N, H, 128, 128, device=dev) * 0.1,
+                        }
+                        sets.append((inp, kda.alloc_outputs(w, dev)))
+                    res = {}
+                    for tile, pol in combos + [(0, 0)]:
+                        p = kda.params_for(w, tile_columns=tile, store_policy=pol)
+                        ws = kda.alloc_workspace(p, dev)
+                        for i in range(2 * nset):
+                            kda.run(p, sets[i % nset][0], sets[i % nset][1], ws)
+                        reps = max(8, 2 * nset)
+                        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                              for _ in range(reps)]
+                        for i in range(reps):
+                            ev[i][0].record()
+                            kda.run(p, sets[i % nset][0], sets[i % nset][1], ws)
+                            ev[i][1].record()
+                        torch.cuda.synchronize()
+                        ms = sorted(a.elapsed_time(b) for a, b in ev)
+                        res[f"{tile}/{pol}" if tile else "auto"] = ms[len(ms) // 2]
+                    best = min((v, k) for k, v in res.items() if k != "auto")
+                    auto_p = kda.params_for(w)
+                    row = {"H": H, "T": T, "N": N, "units": N * H, "bytes": b_alg, "ms": res,
+                           "best": best[1], "best_pct": 100 * b_alg / best[0] / 1e6 / HBM_PEAK_GBPS,
+                           "auto_variant": kda.select_variant(auto_p),
+                           "auto_over_best": res["auto"] / best[0]}
+                    rows.append(row)
+                    f.write(json.dumps(row) + "\n")
+                    f.flush()
+                    print(f"H={H:3d} T={T} N={N:4d} units={N * H:6d} best={best[1]:7s} "
+                          f"{row['best_pct']:5.1f}% auto/best={row['auto_over_best']:.3f}", flush=True)
+                    del sets
+                    torch.cuda.empty_cache()
+    worst = max(rows, key=lambda r: r["auto_over_best"])
+    print(f"auto within {100 * (worst['auto_over_best'] - 1):.1f}% of the best combo on every shape "
+          f"(worst: H={worst['H']} T={worst['T']} N={worst['N']})", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--device-warmup", type=float, default=0.3,
+                    help="seconds of untimed calls before the warm-up steps (clock and power ramp)")
     ap.add_argument("--workload", default="large_batch")
     ap.add_argument("--variant", default="auto", choices=["auto", "small", "large"])
     ap.add_argument("--op", default="verify", choices=["verify", "verify_pooled", "commit"],
                     help="verify (the headline), verify on pooled buffers with scattered rows, or the accept step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
+                    help="run the H x T x N sweep over tile widths and store policies instead")
+    ap.add_argument("--sweep-quick", action="store_true", help="a reduced sweep grid")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -104,6 +180,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.sweep:
+        sweep(args.sweep, args.sweep_quick)
+        return
 
     if args.copy_calibration:
         n = 1 << 28  # 2**28 fp32 = 1 GiB
@@ -161,6 +241,15 @@ def main():
             s_in = 2 if w.dtype == "bf16" else 4
             b_alg = w.N * (2 * 4 * w.HV * w.K * w.V + 2 * 3 * s_in * w.C) + 4 * 4 * w.N
 
+    # The part ramps its clocks over the first tens of milliseconds of sustained work: run
+    # untimed calls for --device-warmup seconds first (reported as device_warmup_calls).
+    dw_calls = 0
+    t_end = time.perf_counter() + args.device_warmup
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        dw_calls += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -199,6 +288,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "device_warmup_calls": dw_calls,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -80,6 +80,12 @@ typedef struct {
   float softplus_threshold; /* default 20.0 */
   float scale;              /* q scale; <= 0 selects K^-1/2 */
   float l2norm_eps;         /* q/k l2norm: x / sqrt(sum x^2 + eps); default 1e-6, >= 0 */
+  /* Tuning overrides (0 = chosen from the shape). They change speed only, never results:
+   * every tile width and store policy gives the same bits. */
+  int32_t tile_columns;     /* V columns per workgroup: 32, 64 or 128 (K = V = 128 only);
+                               V selects LARGE, fewer SMALL, and overrides `variant` */
+  int32_t store_policy;     /* snapshot stores: 1 streaming (non-temporal), 2 write-through
+                               at device scope */
 } kda_verify_params;
 
 #define KDA_MAX_T 16

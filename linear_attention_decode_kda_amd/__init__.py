@@ -42,6 +42,7 @@ class Params(ctypes.Structure):
         ("gate_mode", ctypes.c_int32), ("variant", ctypes.c_int32),
         ("lower_bound", ctypes.c_float), ("softplus_beta", ctypes.c_float),
         ("softplus_threshold", ctypes.c_float), ("scale", ctypes.c_float), ("l2norm_eps", ctypes.c_float),
+        ("tile_columns", ctypes.c_int32), ("store_policy", ctypes.c_int32),
     ]
 
 
@@ -108,7 +109,7 @@ def lib_status_string(status: int) -> str:
 def make_params(N: int, T: int, H: int, HV: int, K: int, V: int, *, dtype: str = "bf16",
                 gate: str = "softplus", variant: int = VARIANT_AUTO, lower_bound: float = -5.0,
                 softplus_beta: float = 1.0, softplus_threshold: float = 20.0, scale: float = 0.0,
-                l2norm_eps: float = 1e-6) -> Params:
+                l2norm_eps: float = 1e-6, tile_columns: int = 0, store_policy: int = 0) -> Params:
     p = Params()
     load().kda_verify_params_init(ctypes.byref(p), N, T, H, HV, K, V)
     p.in_dtype = {"f32": F32, "bf16": BF16}[dtype]
@@ -119,6 +120,8 @@ def make_params(N: int, T: int, H: int, HV: int, K: int, V: int, *, dtype: str =
     p.softplus_threshold = softplus_threshold
     p.scale = scale
     p.l2norm_eps = l2norm_eps
+    p.tile_columns = tile_columns
+    p.store_policy = store_policy
     return p
 
 

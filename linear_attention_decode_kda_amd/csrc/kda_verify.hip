@@ -668,30 +668,43 @@ hipError_t launch(const Args& a, hipStream_t stream) {
                          dim3(CF::NTHR), args, 0, stream);
 }
 
-// Tile shape and store policy per (K, V), variant and workload, measured on MI355X with
-// the fused step's own traffic (about 1 byte read per 4 written at T = 4):
-//   LARGE: one WG per (n, hv) covering all V columns.
-//   SMALL: V split over several WGs; more, shorter WGs shrink the tail of big grids and
-//          fill the chip for small ones.
-//   agent-coherent (sc1) snapshot stores win when snapshots dominate even more (T >= 8)
-//   or the whole working set stays in the 256 MB last-level cache (small batches);
-//   streaming (nt) stores win otherwise.
-// Every shape uses the same K split (32 rows per wave) and the same partial-sum tree,
+// Tile shape and store policy, from an H = HV x T x N sweep on MI355X (K = V = 128, bf16,
+// every tile width and store policy timed on each shape, buffers rotated so that each
+// run reads and writes HBM):
+//   <= 128 (sequence, value head) units: the whole-V tile, except at T >= 6 where the
+//     32-column split (4 WGs per unit) keeps 4x more WGs busy through the long token loop;
+//   up to 4096 units: the whole-V tile; write-through stores from T = 4;
+//   >= 4096 units: whole V at T <= 2, the 32-column split at T <= 6 (shorter WGs trim the
+//     tail of the grid), whole V with write-through stores at T >= 8.
+// Every tile width uses the same K split (32 rows per wave) and the same partial-sum tree,
 // so all of them return bit-identical results.
 struct Tile {
   int vt;   // V columns per WG
   int stp;  // StorePolicy
 };
 
-Tile choose_tile(int K, int V, int variant, int N, int T, int HV) {
-  const long long units = (long long)N * HV;
+Tile auto_tile_128(long long units, int T) {
+  if (units <= 128) return T >= 6 ? Tile{32, kStoreNT} : Tile{128, kStoreNT};
+  if (units < 4096) return Tile{128, T >= 4 ? kStoreSC1 : kStoreNT};
+  if (T <= 2) return Tile{128, kStoreNT};
+  if (T <= 6) return Tile{32, kStoreNT};
+  return Tile{128, kStoreSC1};
+}
+
+Tile choose_tile(const kda_verify_params* p) {
+  const int K = p->K, V = p->V;
   if (K == 128 && V == 128) {
-    const bool small_ws = units < 1024;
-    const int stp = (T >= 8 || small_ws) ? kStoreSC1 : kStoreNT;
-    if (variant == KDA_VARIANT_LARGE) return {128, stp};
-    return {small_ws ? 64 : 32, stp};
+    Tile t = auto_tile_128((long long)p->N * p->HV, p->T);
+    if (p->tile_columns != 0)
+      t.vt = p->tile_columns;
+    else if (p->variant == KDA_VARIANT_LARGE)
+      t.vt = 128;
+    else if (p->variant == KDA_VARIANT_SMALL)
+      t.vt = 32;
+    if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreSC1 : kStoreNT;
+    return t;
   }
-  if (K == 64 && V == 64) return {variant == KDA_VARIANT_LARGE ? 64 : 32, kStoreNT};
+  if (K == 64 && V == 64) return {p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT};
   return {16, kStoreNT};
 }
 
@@ -755,6 +768,8 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
   p->softplus_threshold = 20.0f;
   p->scale = 0.0f;
   p->l2norm_eps = 1e-6f;
+  p->tile_columns = 0;
+  p->store_policy = 0;
 }
 
 static kda_status check_params(const kda_verify_params* p) {
@@ -771,6 +786,12 @@ static kda_status check_params(const kda_verify_params* p) {
   if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE) return KDA_ERR_UNSUPPORTED;
   if (p->variant < KDA_VARIANT_AUTO || p->variant > KDA_VARIANT_LARGE) return KDA_ERR_UNSUPPORTED;
   if (!(p->softplus_beta > 0.0f) || !(p->l2norm_eps >= 0.0f) || p->scale != p->scale) return KDA_ERR_SHAPE;
+  if (p->store_policy < 0 || p->store_policy > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->tile_columns != 0) {
+    const bool ok = p->K == 128 && p->V == 128 &&
+                    (p->tile_columns == 32 || p->tile_columns == 64 || p->tile_columns == 128);
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+  }
   return KDA_OK;
 }
 
@@ -784,16 +805,9 @@ size_t kda_workspace_bytes(const kda_verify_params* p) {
 int32_t kda_select_variant(const kda_verify_params* p) {
   kda_status st = check_params(p);
   if (st != KDA_OK) return st;
+  if (p->tile_columns != 0) return p->tile_columns == p->V ? KDA_VARIANT_LARGE : KDA_VARIANT_SMALL;
   if (p->variant != KDA_VARIANT_AUTO) return p->variant;
-  if (p->K < 128) return KDA_VARIANT_LARGE;
-  // Crossovers measured on MI355X (K = V = 128): below 1024 (sequence, value head)
-  // units a whole-V WG per unit leaves CUs idle, so V is split; at T >= 8 the long
-  // write phase favours whole-V WGs; from 4096 units at T < 8 the shorter split WGs
-  // trim the tail of the grid.
-  const long long units = (long long)p->N * p->HV;
-  if (units < 1024) return KDA_VARIANT_SMALL;
-  if (p->T >= 8) return KDA_VARIANT_LARGE;
-  return units >= 4096 ? KDA_VARIANT_SMALL : KDA_VARIANT_LARGE;
+  return choose_tile(p).vt < p->V ? KDA_VARIANT_SMALL : KDA_VARIANT_LARGE;
 }
 
 }  // extern "C"
@@ -906,7 +920,7 @@ kda_status kda_conv_verify_decode_pooled(const kda_verify_params* p, const kda_p
                                   state, o, inter_ssm, conv_window, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
   if (p->N == 0) return KDA_OK;
-  const Tile tl = choose_tile(p->K, p->V, kda_select_variant(p), p->N, p->T, p->HV);
+  const Tile tl = choose_tile(p);
   LaunchFn fn = p->in_dtype == KDA_BF16 ? pick<uint16_t>(p->K, p->V, tl, p->T)
                                         : pick<uint32_t>(p->K, p->V, tl, p->T);
   if (!fn) return KDA_ERR_UNSUPPORTED;

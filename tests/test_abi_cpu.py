@@ -54,7 +54,8 @@ def test_workspace_bytes(lib):
 
 def test_select_variant(lib):
     assert kda.select_variant(kda.make_params(256, 4, 32, 32, 128, 128)) == kda.VARIANT_SMALL
-    assert kda.select_variant(kda.make_params(32, 4, 16, 16, 128, 128)) == kda.VARIANT_SMALL
+    assert kda.select_variant(kda.make_params(32, 4, 16, 16, 128, 128)) == kda.VARIANT_LARGE
+    assert kda.select_variant(kda.make_params(4, 8, 16, 16, 128, 128)) == kda.VARIANT_SMALL
     assert kda.select_variant(kda.make_params(64, 3, 16, 32, 128, 128)) == kda.VARIANT_LARGE
     assert kda.select_variant(kda.make_params(512, 8, 16, 64, 128, 128)) == kda.VARIANT_LARGE
     assert kda.select_variant(kda.make_params(2, 2, 2, 2, 16, 16)) == kda.VARIANT_LARGE
@@ -195,3 +196,17 @@ def test_commit_validation(lib):
     assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -7
     p0 = kda.make_params(0, 4, 2, 4, 128, 128)
     assert lib.kda_verify_commit(ctypes.byref(p0), None, *args([0] * 5), None) == 0
+
+
+def test_tuning_overrides(lib):
+    p = kda.make_params(256, 4, 32, 32, 128, 128, tile_columns=128)
+    assert kda.select_variant(p) == kda.VARIANT_LARGE
+    p = kda.make_params(8, 4, 2, 2, 128, 128, tile_columns=32, variant=kda.VARIANT_LARGE)
+    assert kda.select_variant(p) == kda.VARIANT_SMALL  # the tile override wins
+    for bad in (dict(tile_columns=48), dict(store_policy=3)):
+        p = kda.make_params(8, 4, 2, 2, 128, 128, **bad)
+        ptrs, wsb = _fake_ptrs(p)
+        assert _validate(lib, p, ptrs, wsb) == -3
+    p = kda.make_params(8, 4, 2, 2, 64, 64, tile_columns=64)  # overrides exist for K = V = 128 only
+    ptrs, wsb = _fake_ptrs(p)
+    assert _validate(lib, p, ptrs, wsb) == -3

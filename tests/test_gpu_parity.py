@@ -231,12 +231,12 @@ def test_zero_q_k_channels():
     assert torch.count_nonzero(got["o"]) == 0
 
 
-@pytest.mark.parametrize("w", [W(64, 2, 64, 64, 128, 128, gate="safe"),   # 4096 units: split V in 32-column WGs
-                               W(16, 3, 8, 16, 128, 128),                  # 256 units: 64-column WGs, sc1 stores
-                               W(32, 8, 16, 32, 128, 128, gate="safe")])   # T = 8: sc1 stores in both variants
+@pytest.mark.parametrize("w", [W(64, 2, 64, 64, 128, 128, gate="safe"),   # 4096 units, streaming stores
+                               W(16, 4, 8, 16, 128, 128),                  # 256 units, write-through stores
+                               W(32, 8, 16, 32, 128, 128, gate="safe")])   # T = 8, write-through stores
 def test_every_tile_shape_bit_identical(w):
-    """Whatever tile shape and store policy dispatch picks, the results are the same bits;
-    a sample of sequences is also checked against the oracle."""
+    """SMALL (32-column WGs) and LARGE (whole-V WGs) with the store policy dispatch picks for
+    the shape give the same bits; a sample of sequences is also checked against the oracle."""
     inp = synth.make_inputs(w)
     a = run_gpu(w, inp, S)
     b = run_gpu(w, inp, L)
@@ -245,3 +245,18 @@ def test_every_tile_shape_bit_identical(w):
     sample = np.array([0, w.N - 1])
     ref = oracle.verify_workload(w.with_(N=2), slice_inputs(inp, sample))
     assert_matches(w, a, ref, n_index=sample, what=f"tile shapes {w.name}")
+
+
+def test_explicit_tile_and_store_overrides_bit_identical():
+    """Every tile width (32, 64, 128 columns per WG) and both snapshot store policies give
+    the same bits; one of them is checked against the oracle."""
+    w = W(5, 3, 2, 4, 128, 128, gate="safe")
+    inp = synth.make_inputs(w)
+    outs = []
+    for tile in (32, 64, 128):
+        for pol in (1, 2):
+            outs.append(run_gpu(w, inp, A, tile_columns=tile, store_policy=pol))
+    for o in outs[1:]:
+        for k in ("o", "inter_ssm", "conv_window", "conv_state"):
+            assert torch.equal(o[k], outs[0][k]), k
+    assert_matches(w, outs[0], oracle.verify_workload(w, inp), what="overrides")
