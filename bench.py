@@ -157,8 +157,9 @@ def main():
                     help="seconds of untimed calls before the warm-up steps (clock and power ramp)")
     ap.add_argument("--workload", default="large_batch")
     ap.add_argument("--variant", default="auto", choices=["auto", "small", "large"])
-    ap.add_argument("--op", default="verify", choices=["verify", "verify_pooled", "commit"],
-                    help="verify (the headline), verify on pooled buffers with scattered rows, or the accept step")
+    ap.add_argument("--op", default="verify", choices=["verify", "verify_pooled", "commit", "unfused"],
+                    help="verify (the headline), verify on pooled buffers with scattered rows, the accept "
+                         "step, or the unfused two-kernel form of verify (same algorithmic bytes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
@@ -211,6 +212,14 @@ def main():
         def step():
             kda.run(p, inp, out, ws, stream)
         b_alg = synth.algorithmic_bytes(w)
+    elif args.op == "unfused":
+        act = torch.empty((w.N, w.T, w.C), dtype=torch.float32, device=dev)
+
+        def step():
+            kda.kda_conv_verify_decode_unfused(p, None, inp["mixed_qkv"], inp["conv_weight"], inp["conv_state"],
+                                               inp["gate"], inp["A_log"], inp["dt_bias"], inp["beta"], inp["state"],
+                                               out["o"], out["inter_ssm"], out["conv_window"], act, ws, stream)
+        b_alg = synth.algorithmic_bytes(w)  # the fused step's bytes, so the fractions compare directly
     else:
         # pools twice the batch, sequence rows scattered by a seeded permutation
         g = torch.Generator().manual_seed(w.seed)

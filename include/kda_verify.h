@@ -172,6 +172,22 @@ kda_status kda_conv_verify_decode_pooled(const kda_verify_params* p, const kda_p
                                          void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 
+/* The same step in unfused form, for measuring what fusion saves (PR#107 PR description:
+ * fusing removes a separate conv launch and intermediate HBM round trips). A first kernel
+ * runs the conv + SiLU over all channels and writes the activations to act [N,T,C]
+ * (fp32), the conv windows and the rolled cache; a second kernel runs the rest of the
+ * step from act. Same arguments, pools and validation as kda_conv_verify_decode_pooled,
+ * plus act (device, 16-byte aligned, not overlapping any other buffer). The activations
+ * stay fp32 so that the results keep the fused step's accuracy (rounding them to bf16
+ * moves inter_ssm by up to ~6e-3). */
+kda_status kda_conv_verify_decode_unfused(const kda_verify_params* p, const kda_pool_desc* pools,
+                                          const void* mixed_qkv, const void* conv_weight,
+                                          void* conv_state, const void* gate, const float* A_log,
+                                          const float* dt_bias, const void* beta, const float* state,
+                                          void* o, float* inter_ssm, void* conv_window, void* act,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
 /* Accept step after a verify (PR#107 PR description: the per-token snapshots exist so the
  * caller can roll back to the accepted prefix). accepted [N] (device int32) holds a_n,
  * the number of tokens of sequence n that were kept, 1 <= a_n <= T. For each such n:

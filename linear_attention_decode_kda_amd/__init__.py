@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
     PD = ctypes.POINTER(PoolDesc)
     lib.kda_conv_verify_decode_pooled.argtypes = [PP, PD] + [_VP] * 12 + [_SZ, _VP]
     lib.kda_conv_verify_decode_pooled.restype = ctypes.c_int
+    lib.kda_conv_verify_decode_unfused.argtypes = [PP, PD] + [_VP] * 13 + [_SZ, _VP]
+    lib.kda_conv_verify_decode_unfused.restype = ctypes.c_int
     lib.kda_verify_commit.argtypes = [PP, PD] + [_VP] * 5 + [_VP]
     lib.kda_verify_commit.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int32]
@@ -253,6 +255,37 @@ def kda_conv_verify_decode_pooled(p: Params, pools: PoolDesc, mixed_qkv, conv_we
                                               workspace.numel() * workspace.element_size(), _VP(_stream(stream)))
     if st != KDA_OK:
         raise KdaError(st, "kda_conv_verify_decode_pooled")
+
+
+def kda_conv_verify_decode_unfused(p: Params, pools: Optional[PoolDesc], mixed_qkv, conv_weight, conv_state, gate,
+                                   A_log, dt_bias, beta, state, o, inter_ssm, conv_window, act, workspace,
+                                   stream=None) -> None:
+    """The step in unfused form (separate conv kernel, fp32 activations through ``act`` [N,T,C])."""
+    N, T, H, HV, K, V = p.N, p.T, p.H, p.HV, p.K, p.V
+    C = 2 * H * K + HV * V
+    dt = _TORCH_DT.get(p.in_dtype)
+    if dt is None:
+        raise KdaError(-3, "kda_conv_verify_decode_unfused")
+    if pools is None:
+        pools = make_pools(N)
+    _check("mixed_qkv", mixed_qkv, (N, T, C), dt)
+    _check("conv_weight", conv_weight, (C, 4), dt)
+    _check("conv_state", conv_state, (pools.conv_state_slots, C, 3), dt)
+    _check("gate", gate, (N, T, HV, K), dt)
+    _check("A_log", A_log, (HV,), torch.float32)
+    _check("dt_bias", dt_bias, (HV * K,), torch.float32)
+    _check("beta", beta, (N, T, HV), dt)
+    _check("state", state, (pools.state_slots, HV, K, V), torch.float32)
+    _check("o", o, (N, T, HV, V), dt)
+    _check("inter_ssm", inter_ssm, (pools.intermediate_slots, T, HV, K, V), torch.float32)
+    _check("conv_window", conv_window, (pools.intermediate_slots, T, C, 3), dt)
+    _check("act", act, (N, T, C), torch.float32)
+    ptrs = [t.data_ptr() for t in (mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
+                                   o, inter_ssm, conv_window, act, workspace)]
+    st = load().kda_conv_verify_decode_unfused(ctypes.byref(p), ctypes.byref(pools), *[_VP(x) for x in ptrs],
+                                               workspace.numel() * workspace.element_size(), _VP(_stream(stream)))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_conv_verify_decode_unfused")
 
 
 def verify_commit(p: Params, pools: PoolDesc, accepted, inter_ssm, conv_window, state, conv_state,

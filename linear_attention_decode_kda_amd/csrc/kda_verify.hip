@@ -42,6 +42,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "kda_verify.h"
 
 namespace kda {
@@ -187,9 +189,12 @@ struct Args {
 // Snapshot store cache policy: streaming (nt) or agent-coherent write-through (sc1).
 enum StorePolicy { kStoreNT = 0, kStoreSC1 = 1 };
 
-template <typename R, int K_, int V_, int VT_, int NW_, int TMAX_, int STP_ = kStoreNT>
+// PRE_ = 1: the unfused form of the step. The conv + SiLU ran in a separate kernel and
+// mixed_qkv holds its fp32 activations; this kernel only stages them (no conv cache, no
+// taps, no conv-window or conv-state writes).
+template <typename R, int K_, int V_, int VT_, int NW_, int TMAX_, int STP_ = kStoreNT, int PRE_ = 0>
 struct Cfg {
-  static constexpr int K = K_, V = V_, VT = VT_, NW = NW_, TMAX = TMAX_, STP = STP_;
+  static constexpr int K = K_, V = V_, VT = VT_, NW = NW_, TMAX = TMAX_, STP = STP_, PRE = PRE_;
   static constexpr int NTHR = NW * 64;
   static constexpr int NVT = V / VT;     // WGs per (n, hv)
   static constexpr int RW = K / NW;      // K rows per wave
@@ -202,11 +207,13 @@ struct Cfg {
   static constexpr int LOGP = P == 8 ? 3 : 4;
   static constexpr int NCH = 2 * K + VT;        // channels a WG stages: q, k, its v columns
   static constexpr int E16 = 16 / (int)sizeof(R);  // elements per 16-byte vector
+  using XR = typename std::conditional<PRE_ != 0, uint32_t, R>::type;  // staged token rows
+  static constexpr int XE16 = 16 / (int)sizeof(XR);
   static_assert(V % VT == 0 && VT % 4 == 0 && 64 % LPR == 0 && K % NW == 0, "tile shape");
   static_assert(RW % Q == 0 && P % Q == 0 && RPL % M == 0 && (1 << LOGQ) == Q && RW % P == 0, "rows");
   static_assert(K % E16 == 0 && VT % E16 == 0 && K % 4 == 0 && K <= 128, "vector widths");
   // 16-byte vectors staged per WG at T = TMAX
-  static constexpr int MAX_CHUNKS = TMAX * NCH / E16 + 3 * NCH / E16 + 4 * NCH / E16 + TMAX * K / E16 + K / 4;
+  static constexpr int MAX_CHUNKS = TMAX * NCH / XE16 + 3 * NCH / E16 + 4 * NCH / E16 + TMAX * K / E16 + K / 4;
   static constexpr int MAXC = (MAX_CHUNKS + NTHR - 1) / NTHR;
 };
 
@@ -222,7 +229,7 @@ struct alignas(16) Smem {
   f32x4 part[2][CF::NW][2][CF::LPR];  // per-wave partial sums (u, w), double-buffered by token
   float betas[CF::TMAX];
   float qk[CF::TMAX];
-  alignas(16) R xs[CF::TMAX * CF::NCH];  // raw new tokens, [t][local channel]
+  alignas(16) typename CF::XR xs[CF::TMAX * CF::NCH];  // raw new tokens, [t][local channel]
   alignas(16) R cs[3 * CF::NCH];         // raw conv cache, [local channel][3]
   alignas(16) R ws[4 * CF::NCH];         // conv taps, [local channel][4]
   alignas(16) R gs[CF::TMAX * CF::K];    // raw gate, [t][K]
@@ -302,17 +309,17 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
       in_row >= a.in_slots)
     return;  // padding entry: the whole WG (and its group) skips, nothing is read or written
 
-  const R* __restrict__ xq = static_cast<const R*>(a.mixed_qkv);
+  const typename CF::XR* __restrict__ xq = static_cast<const typename CF::XR*>(a.mixed_qkv);
   const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
   R* cstate = static_cast<R*>(a.conv_state);
   const R* __restrict__ gq = static_cast<const R*>(a.gate);
   const R* __restrict__ bq = static_cast<const R*>(a.beta);
 
   // ---------------- prologue: issue every 16-byte load of the WG's small inputs
-  const int PA = NCH / E16;
+  const int PA = NCH / CF::XE16;
   const int nA = T * PA;              // new tokens
-  const int nB = 3 * NCH / E16;       // conv cache
-  const int nC = 4 * NCH / E16;       // conv taps
+  const int nB = CF::PRE ? 0 : 3 * NCH / E16;  // conv cache
+  const int nC = CF::PRE ? 0 : 4 * NCH / E16;  // conv taps
   const int nD = T * K / E16;         // gate
   const int nE = K / 4;               // dt_bias (fp32)
   const int total = nA + nB + nC + nD + nE;
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     const void* src;
     int dst;
     if (ci < nA) {
-      const int t = ci / PA, pe = (ci - t * PA) * E16;
+      const int t = ci / PA, pe = (ci - t * PA) * CF::XE16;
       src = xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt);
       dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
     } else if ((ci -= nA) < nB) {
@@ -374,17 +381,22 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   // q/k conv-cache ownership: count this WG in now (its reads have landed); the count
   // is read only after the prologue math, so nothing waits on the atomic until then.
   uint32_t prev = 0;
-  if (tid == 0 && a.group > 1)
+  if (!CF::PRE && tid == 0 && a.group > 1)
     prev = __hip_atomic_fetch_add(a.counters + (size_t)n * H + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---------------- phase 1a: conv + SiLU, one task per (token, staged channel)
   for (int task = tid; task < T * NCH; task += NTHR) {
     const int t = task / NCH, ch = task - (task / NCH) * NCH;
-    const float y = fmaf(up(s.ws[ch * 4 + 3]), up(ext_raw<CF, R>(s, ch, t + 3)),
-                         fmaf(up(s.ws[ch * 4 + 2]), up(ext_raw<CF, R>(s, ch, t + 2)),
-                              fmaf(up(s.ws[ch * 4 + 1]), up(ext_raw<CF, R>(s, ch, t + 1)),
-                                   up(s.ws[ch * 4 + 0]) * up(ext_raw<CF, R>(s, ch, t)))));
-    const float act = silu_fast(y);
+    float act;
+    if constexpr (CF::PRE) {
+      act = up(s.xs[t * NCH + ch]);  // already convolved and activated
+    } else {
+      const float y = fmaf(up(s.ws[ch * 4 + 3]), up(ext_raw<CF, R>(s, ch, t + 3)),
+                           fmaf(up(s.ws[ch * 4 + 2]), up(ext_raw<CF, R>(s, ch, t + 2)),
+                                fmaf(up(s.ws[ch * 4 + 1]), up(ext_raw<CF, R>(s, ch, t + 1)),
+                                     up(s.ws[ch * 4 + 0]) * up(ext_raw<CF, R>(s, ch, t)))));
+      act = silu_fast(y);
+    }
     if (ch < K)
       s.row[row_slot<CF>(t, ch)].y = act;  // q, normalised in phase 2
     else if (ch < 2 * K)
@@ -554,6 +566,8 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     }
   }
 
+  if constexpr (CF::PRE) return;  // the conv kernel wrote the windows and the rolled cache
+
   // ---------------- raw copies, issued last so that no wait for them ever precedes the
   // token loop: conv windows (v columns always; q/k by one WG per group), the rolled
   // conv cache of the v columns (read only by this WG), and the rolled cache of the
@@ -600,6 +614,56 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
       put_window_vec<CF, R>(s, cstate + ((size_t)cs_row * C + gc0) * 3, seg * K, -1, T, m);
     }
   }
+}
+
+// Unfused form, first kernel: width-4 causal conv + SiLU for every channel, one thread per
+// (sequence, channel) walking the T tokens with a 3-value raw window; writes the fp32
+// activations to act [N,T,C], the per-token raw windows and the rolled cache.
+struct ConvArgs {
+  const void* x;
+  const void* w;
+  void* conv_state;
+  void* conv_window;
+  void* act;
+  const int32_t* cs_idx;
+  const int32_t* st_idx;
+  const int32_t* in_idx;
+  int cs_slots, st_slots, in_slots;
+  int N, T, C;
+};
+
+template <typename R>
+__global__ __launch_bounds__(256) void kda_conv_silu_kernel(const ConvArgs a) {
+  const int n = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.C) return;
+  const int cs_row = a.cs_idx ? a.cs_idx[n] : n;
+  const int st_row = a.st_idx ? a.st_idx[n] : n;
+  const int in_row = a.in_idx ? a.in_idx[n] : n;
+  if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
+      in_row >= a.in_slots)
+    return;
+  const R* x = static_cast<const R*>(a.x);
+  const R* w = static_cast<const R*>(a.w) + (size_t)c * 4;
+  R* cs = static_cast<R*>(a.conv_state) + ((size_t)cs_row * a.C + c) * 3;
+  R* cw = static_cast<R*>(a.conv_window);
+  float* act = static_cast<float*>(a.act);
+  const float w0 = up(w[0]), w1 = up(w[1]), w2 = up(w[2]), w3 = up(w[3]);
+  R e0 = cs[0], e1 = cs[1], e2 = cs[2];
+  for (int t = 0; t < a.T; ++t) {
+    const R e3 = x[((size_t)n * a.T + t) * a.C + c];
+    const float y = fmaf(w3, up(e3), fmaf(w2, up(e2), fmaf(w1, up(e1), w0 * up(e0))));
+    act[((size_t)n * a.T + t) * a.C + c] = silu_fast(y);
+    R* wrow = cw + (((size_t)in_row * a.T + t) * a.C + c) * 3;
+    wrow[0] = e1;
+    wrow[1] = e2;
+    wrow[2] = e3;
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
+  }
+  cs[0] = e0;
+  cs[1] = e1;
+  cs[2] = e2;
 }
 
 // Accept step: one WG per (sequence, value head) copies the state snapshot of the last
@@ -715,31 +779,37 @@ Tile choose_tile(const kda_verify_params* p) {
   return {16, kStoreNT};
 }
 
-template <typename R, int TMAX>
+template <typename R, int TMAX, int PRE>
 LaunchFn pick_tmax(int K, int V, Tile tl) {
   if (K == 128 && V == 128) {
     if (tl.vt == 128)
-      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1>, R>
-                                 : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT>, R>;
+      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1, PRE>, R>
+                                 : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT, PRE>, R>;
     if (tl.vt == 64)
-      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1>, R>
-                                 : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT>, R>;
-    return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreSC1>, R>
-                               : &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNT>, R>;
+      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1, PRE>, R>
+                                 : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT, PRE>, R>;
+    return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreSC1, PRE>, R>
+                               : &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNT, PRE>, R>;
   }
   if (K == 64 && V == 64) {
-    if (tl.vt == 64) return &launch<Cfg<R, 64, 64, 64, 2, TMAX>, R>;
-    return &launch<Cfg<R, 64, 64, 32, 2, TMAX>, R>;
+    if (tl.vt == 64) return &launch<Cfg<R, 64, 64, 64, 2, TMAX, kStoreNT, PRE>, R>;
+    return &launch<Cfg<R, 64, 64, 32, 2, TMAX, kStoreNT, PRE>, R>;
   }
-  if (K == 16 && V == 16) return &launch<Cfg<R, 16, 16, 16, 1, TMAX>, R>;
+  if (K == 16 && V == 16) return &launch<Cfg<R, 16, 16, 16, 1, TMAX, kStoreNT, PRE>, R>;
   return nullptr;
 }
 
-template <typename R>
+template <typename R, int PRE>
 LaunchFn pick(int K, int V, Tile tl, int T) {
-  if (T <= 4) return pick_tmax<R, 4>(K, V, tl);
-  if (T <= 8) return pick_tmax<R, 8>(K, V, tl);
-  return pick_tmax<R, 16>(K, V, tl);
+  if (T <= 4) return pick_tmax<R, 4, PRE>(K, V, tl);
+  if (T <= 8) return pick_tmax<R, 8, PRE>(K, V, tl);
+  return pick_tmax<R, 16, PRE>(K, V, tl);
+}
+
+LaunchFn pick_launch(const kda_verify_params* p, Tile tl, bool pre) {
+  if (p->in_dtype == KDA_BF16)
+    return pre ? pick<uint16_t, 1>(p->K, p->V, tl, p->T) : pick<uint16_t, 0>(p->K, p->V, tl, p->T);
+  return pre ? pick<uint32_t, 1>(p->K, p->V, tl, p->T) : pick<uint32_t, 0>(p->K, p->V, tl, p->T);
 }
 
 bool supported_kv(int K, int V) { return K == V && (K == 16 || K == 64 || K == 128); }
@@ -866,6 +936,11 @@ bool any_alias(const Range* in, size_t nin, const Range* out, size_t nout) {
   return false;
 }
 
+kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const void* mixed_qkv,
+                         const void* conv_weight, void* conv_state, const void* gate, const float* A_log,
+                         const float* dt_bias, const void* beta, const float* state, void* o, float* inter_ssm,
+                         void* conv_window, void* workspace, hipStream_t stream, bool pre);
+
 kda_status validate_verify(const kda_verify_params* p, const kda_pool_desc* pools, PoolView* pv,
                            const void* mixed_qkv, const void* conv_weight, const void* conv_state, const void* gate,
                            const float* A_log, const float* dt_bias, const void* beta, const float* state,
@@ -927,9 +1002,19 @@ kda_status kda_conv_verify_decode_pooled(const kda_verify_params* p, const kda_p
                                   state, o, inter_ssm, conv_window, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
   if (p->N == 0) return KDA_OK;
-  const Tile tl = choose_tile(p);
-  LaunchFn fn = p->in_dtype == KDA_BF16 ? pick<uint16_t>(p->K, p->V, tl, p->T)
-                                        : pick<uint32_t>(p->K, p->V, tl, p->T);
+  return launch_verify(p, pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o, inter_ssm,
+                       conv_window, workspace, stream, false);
+}
+
+}  // extern "C"
+
+namespace kda {
+
+kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const void* mixed_qkv,
+                         const void* conv_weight, void* conv_state, const void* gate, const float* A_log,
+                         const float* dt_bias, const void* beta, const float* state, void* o, float* inter_ssm,
+                         void* conv_window, void* workspace, hipStream_t stream, bool pre) {
+  LaunchFn fn = pick_launch(p, choose_tile(p), pre);
   if (!fn) return KDA_ERR_UNSUPPORTED;
   Args a;
   a.mixed_qkv = mixed_qkv;
@@ -964,6 +1049,60 @@ kda_status kda_conv_verify_decode_pooled(const kda_verify_params* p, const kda_p
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->K);
   a.eps = p->l2norm_eps;
   return fn(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace kda
+
+extern "C" {
+
+kda_status kda_conv_verify_decode_unfused(const kda_verify_params* p, const kda_pool_desc* pools,
+                                          const void* mixed_qkv, const void* conv_weight, void* conv_state,
+                                          const void* gate, const float* A_log, const float* dt_bias,
+                                          const void* beta, const float* state, void* o, float* inter_ssm,
+                                          void* conv_window, void* act, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  PoolView pv;
+  kda_status st = validate_verify(p, pools, &pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta,
+                                  state, o, inter_ssm, conv_window, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  if (p->N == 0) return KDA_OK;
+  if (!act) return KDA_ERR_NULL;
+  if (misaligned(act)) return KDA_ERR_ALIGN;
+  const size_t s = p->in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t C = 2 * (size_t)p->H * p->K + (size_t)p->HV * p->V;
+  const Range act_r = rg(act, 4 * (size_t)p->N * p->T * C);
+  const void* others[] = {mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o, inter_ssm,
+                          conv_window, workspace};
+  const size_t sizes[] = {s * p->N * p->T * C, s * C * 4, s * pv.cs_slots * C * 3, s * p->N * p->T * p->HV * p->K,
+                          4 * (size_t)p->HV, 4 * (size_t)p->HV * p->K, s * p->N * p->T * p->HV,
+                          4 * pv.st_slots * p->HV * p->K * p->V, s * p->N * p->T * p->HV * p->V,
+                          4 * pv.in_slots * p->T * p->HV * p->K * p->V, s * pv.in_slots * p->T * C * 3,
+                          kda_workspace_bytes(p)};
+  for (size_t i = 0; i < sizeof(others) / sizeof(others[0]); ++i)
+    if (overlap(act_r, rg(others[i], sizes[i]))) return KDA_ERR_ALIAS;
+  ConvArgs c;
+  c.x = mixed_qkv;
+  c.w = conv_weight;
+  c.conv_state = conv_state;
+  c.conv_window = conv_window;
+  c.act = act;
+  c.cs_idx = pv.cs_idx;
+  c.st_idx = pv.st_idx;
+  c.in_idx = pv.in_idx;
+  c.cs_slots = (int)pv.cs_slots;
+  c.st_slots = (int)pv.st_slots;
+  c.in_slots = (int)pv.in_slots;
+  c.N = p->N;
+  c.T = p->T;
+  c.C = (int)C;
+  void* cargs[] = {&c};
+  const void* ck = p->in_dtype == KDA_BF16 ? reinterpret_cast<const void*>(&kda_conv_silu_kernel<uint16_t>)
+                                           : reinterpret_cast<const void*>(&kda_conv_silu_kernel<uint32_t>);
+  if (hipLaunchKernel(ck, dim3((unsigned)((C + 255) / 256), (unsigned)p->N), dim3(256), cargs, 0, stream) !=
+      hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return launch_verify(p, pv, act, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o, inter_ssm,
+                       conv_window, workspace, stream, true);
 }
 
 kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
