@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--op", default="verify", choices=["verify", "verify_pooled", "commit", "unfused"],
                     help="verify (the headline), verify on pooled buffers with scattered rows, the accept "
                          "step, or the unfused two-kernel form of verify (same algorithmic bytes)")
+    ap.add_argument("--tile", type=int, default=0, help="override: V columns per workgroup (32, 64, 128)")
+    ap.add_argument("--store", type=int, default=0, help="override: snapshot stores, 1 streaming, 2 write-through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
@@ -198,7 +200,7 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     variant = {"auto": kda.VARIANT_AUTO, "small": kda.VARIANT_SMALL, "large": kda.VARIANT_LARGE}[args.variant]
-    p = kda.params_for(w, variant=variant)
+    p = kda.params_for(w, variant=variant, tile_columns=args.tile, store_policy=args.store)
     resolved = {kda.VARIANT_SMALL: "small", kda.VARIANT_LARGE: "large"}[kda.select_variant(p)]
     print(f"[bench] workload={w.name} N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V} "
           f"{w.dtype} {w.gate} variant={resolved}", file=sys.stderr, flush=True)
