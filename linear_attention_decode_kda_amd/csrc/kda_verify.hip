@@ -137,18 +137,6 @@ __device__ __forceinline__ void store_snapshot(float* p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
 
-// x + x[lane ^ (LPR << bit)]; bit is a compile-time constant after unrolling
-template <int LPR>
-__device__ __forceinline__ float xor_sum_dyn(float x, int bit) {
-  const int mask = LPR << bit;
-  if (mask == 1) return xor_sum<1>(x);
-  if (mask == 2) return xor_sum<2>(x);
-  if (mask == 4) return xor_sum<4>(x);
-  if (mask == 8) return xor_sum<8>(x);
-  if (mask == 16) return xor_sum<16>(x);
-  return xor_sum<32>(x);
-}
-
 // Workgroups are handed to the 8 XCDs round-robin by blockIdx. Map blockIdx so that
 // each XCD works through one contiguous range of units: the WGs sharing an XCD's L2 then
 // stream through neighbouring state and snapshot addresses. A bijection on [0, B).
@@ -189,6 +177,34 @@ struct Args {
 // Snapshot store cache policy: streaming (nt) or agent-coherent write-through (sc1).
 enum StorePolicy { kStoreNT = 0, kStoreSC1 = 1 };
 
+// Partial-sum plan. A wave's P canonical partial sums of each column are paired in a
+// fixed order of their index bits (1, 2, 0, then 3 when P = 16), the same for every tile
+// shape, so that every variant forms the same sum. Index bits below LOGQ are lane bits
+// (partner lane ^ (LPR << bit)), the others pair partials held by one lane. A lane level
+// at lane distance 16 or 32 is a permlane swap that also halves the values each lane
+// carries (one swap serves two sums); a shorter one is an all-reduce, after which the two
+// lanes hold the same values (their distance bits form the DUP mask).
+constexpr int plan_bit(int lv) { return lv == 0 ? 1 : lv == 1 ? 2 : lv == 2 ? 0 : 3; }
+constexpr bool plan_halves(int lv, int logq, int lpr) {
+  return plan_bit(lv) < logq && (lpr << plan_bit(lv)) >= 16;
+}
+constexpr int plan_nhalf(int logp, int logq, int lpr) {
+  int c = 0;
+  for (int l = 0; l < logp; ++l) c += plan_halves(l, logq, lpr) ? 1 : 0;
+  return c;
+}
+constexpr int plan_dup(int logp, int logq, int lpr) {
+  int m = 0;
+  for (int l = 0; l < logp; ++l)
+    if (plan_bit(l) < logq && !plan_halves(l, logq, lpr)) m |= lpr << plan_bit(l);
+  return m;
+}
+constexpr int plan_half_mask(int j, int logp, int logq, int lpr) {  // lane bit of halving j
+  for (int l = 0; l < logp; ++l)
+    if (plan_halves(l, logq, lpr) && j-- == 0) return lpr << plan_bit(l);
+  return 0;
+}
+
 // PRE_ = 1: the unfused form of the step. The conv + SiLU ran in a separate kernel and
 // mixed_qkv holds its fp32 activations; this kernel only stages them (no conv cache, no
 // taps, no conv-window or conv-state writes).
@@ -212,15 +228,63 @@ struct Cfg {
   static_assert(V % VT == 0 && VT % 4 == 0 && 64 % LPR == 0 && K % NW == 0, "tile shape");
   static_assert(RW % Q == 0 && P % Q == 0 && RPL % M == 0 && (1 << LOGQ) == Q && RW % P == 0, "rows");
   static_assert(K % E16 == 0 && VT % E16 == 0 && K % 4 == 0 && K <= 128, "vector widths");
+  // the partial-sum plan of this shape
+  static constexpr int sum_bit(int lv) { return plan_bit(lv); }
+  static constexpr bool halves(int lv) { return plan_halves(lv, LOGQ, LPR); }
+  static constexpr int NHALF = plan_nhalf(LOGP, LOGQ, LPR);
+  static constexpr int DUP = plan_dup(LOGP, LOGQ, LPR);
+  static constexpr int half_mask(int j) { return plan_half_mask(j, LOGP, LOGQ, LPR); }
+  static constexpr int NOUT = 8 >> NHALF;  // (u|w, column) sums a lane ends with
+  static_assert(NHALF <= 3, "halving levels");
   // 16-byte vectors staged per WG at T = TMAX
   static constexpr int MAX_CHUNKS = TMAX * NCH / XE16 + 3 * NCH / E16 + 4 * NCH / E16 + TMAX * K / E16 + K / 4;
   static constexpr int MAXC = (MAX_CHUNKS + NTHR - 1) / NTHR;
 };
 
-// Pairing order of the P per-wave partial sums (bits of the partial index): the same
-// in every tile shape, so every variant forms the same sum.
-__device__ constexpr int kSumOrder8[3] = {1, 2, 0};
-__device__ constexpr int kSumOrder16[4] = {1, 2, 0, 3};
+// Halving step across lanes l and l ^ MASK (MASK 16 or 32): the lane with that bit clear
+// returns a[l] + a[l ^ MASK], the other b[l] + b[l ^ MASK]. One swap serves two sums.
+template <int MASK>
+__device__ __forceinline__ float swap_sum(float a, float b) {
+  static_assert(MASK == 16 || MASK == 32, "swap mask");
+  const auto r = MASK == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reduce a lane's partials acc[m][label] (label = 4 * (w ? 1 : 0) + column) over the P
+// canonical partials of a wave, level LV of the pairing order onward. CNT labels are live;
+// DONE holds the partial-index bits already summed within the lane.
+template <class CF, int LV, int CNT, int DONE>
+__device__ __forceinline__ void reduce_partials(float (&acc)[CF::M][8]) {
+  if constexpr (LV < CF::LOGP) {
+    constexpr int bit = CF::sum_bit(LV);
+    if constexpr (bit >= CF::LOGQ) {  // both partners in this lane
+      constexpr int mb = 1 << (bit - CF::LOGQ);
+#pragma unroll
+      for (int m = 0; m < CF::M; ++m)
+        if ((m & DONE) == 0 && (m & mb) == 0)
+#pragma unroll
+          for (int l = 0; l < CNT; ++l) acc[m][l] += acc[m | mb][l];
+      reduce_partials<CF, LV + 1, CNT, DONE | mb>(acc);
+    } else if constexpr (CF::halves(LV)) {  // partner lane ^ mask, split the labels
+      constexpr int mask = CF::LPR << bit, h = CNT / 2;
+#pragma unroll
+      for (int m = 0; m < CF::M; ++m)
+        if ((m & DONE) == 0)
+#pragma unroll
+          for (int l = 0; l < h; ++l) acc[m][l] = swap_sum<mask>(acc[m][l], acc[m][l + h]);
+      reduce_partials<CF, LV + 1, h, DONE>(acc);
+    } else {  // partner lane ^ mask, both keep every label
+      constexpr int mask = CF::LPR << bit;
+#pragma unroll
+      for (int m = 0; m < CF::M; ++m)
+        if ((m & DONE) == 0)
+#pragma unroll
+          for (int l = 0; l < CNT; ++l) acc[m][l] = xor_sum<mask>(acc[m][l]);
+      reduce_partials<CF, LV + 1, CNT, DONE>(acc);
+    }
+  }
+}
 
 template <class CF, typename R>
 struct alignas(16) Smem {
@@ -478,55 +542,44 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   float* snap = a.inter_ssm + (size_t)row0 * V + col;
   for (int t = 0; t < T; ++t) {
     const f32x4* rw = &s.row[t * K + row0];
-    // per-lane partials: rows row0 + Q*r, partial m = r % M, rows of a partial in order
-    float pu[M][4], pw[M][4];
+    // per-lane partials: rows row0 + Q*r, partial m = r % M, rows of a partial in order;
+    // label c is column c of u, label 4 + c column c of w
+    float acc[M][8];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       const int m = r % M;
       const f32x4 rr = rw[r * Q];
       const f32x4 sv = S[r];
       if (r < M) {
-        pu[m][0] = rr.x * sv.x; pu[m][1] = rr.x * sv.y; pu[m][2] = rr.x * sv.z; pu[m][3] = rr.x * sv.w;
-        pw[m][0] = rr.y * sv.x; pw[m][1] = rr.y * sv.y; pw[m][2] = rr.y * sv.z; pw[m][3] = rr.y * sv.w;
+        acc[m][0] = rr.x * sv.x; acc[m][1] = rr.x * sv.y; acc[m][2] = rr.x * sv.z; acc[m][3] = rr.x * sv.w;
+        acc[m][4] = rr.y * sv.x; acc[m][5] = rr.y * sv.y; acc[m][6] = rr.y * sv.z; acc[m][7] = rr.y * sv.w;
       } else {
-        pu[m][0] = fmaf(rr.x, sv.x, pu[m][0]); pu[m][1] = fmaf(rr.x, sv.y, pu[m][1]);
-        pu[m][2] = fmaf(rr.x, sv.z, pu[m][2]); pu[m][3] = fmaf(rr.x, sv.w, pu[m][3]);
-        pw[m][0] = fmaf(rr.y, sv.x, pw[m][0]); pw[m][1] = fmaf(rr.y, sv.y, pw[m][1]);
-        pw[m][2] = fmaf(rr.y, sv.z, pw[m][2]); pw[m][3] = fmaf(rr.y, sv.w, pw[m][3]);
+        acc[m][0] = fmaf(rr.x, sv.x, acc[m][0]); acc[m][1] = fmaf(rr.x, sv.y, acc[m][1]);
+        acc[m][2] = fmaf(rr.x, sv.z, acc[m][2]); acc[m][3] = fmaf(rr.x, sv.w, acc[m][3]);
+        acc[m][4] = fmaf(rr.y, sv.x, acc[m][4]); acc[m][5] = fmaf(rr.y, sv.y, acc[m][5]);
+        acc[m][6] = fmaf(rr.y, sv.z, acc[m][6]); acc[m][7] = fmaf(rr.y, sv.w, acc[m][7]);
       }
     }
-    // the P partials of a column sit at index Q*m + qq; pair them in the fixed order
-    int done = 0;  // m bits already summed away (compile-time after unrolling)
-#pragma unroll
-    for (int lv = 0; lv < CF::LOGP; ++lv) {
-      const int bit = CF::P == 8 ? kSumOrder8[lv] : kSumOrder16[lv];
-      if (bit >= CF::LOGQ) {  // both partners in this lane
-        const int mb = 1 << (bit - CF::LOGQ);
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          if ((m & done) == 0 && (m & mb) == 0)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              pu[m][c] += pu[m | mb][c];
-              pw[m][c] += pw[m | mb][c];
-            }
-        done |= mb;
-      } else {  // partner in lane ^ (LPR << bit)
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          if ((m & done) == 0)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              pu[m][c] = xor_sum_dyn<LPR>(pu[m][c], bit);
-              pw[m][c] = xor_sum_dyn<LPR>(pw[m][c], bit);
-            }
-      }
-    }
-    // wave partials through LDS, then waves summed in index order
+    reduce_partials<CF, 0, 8, 0>(acc);
+    // wave partials through LDS, then waves summed in index order; the lanes left holding a
+    // distinct group of NOUT labels write it
     const int buf = t & 1;
-    if (qq == 0) {
-      s.part[buf][wave][0][c4] = f32x4{pu[0][0], pu[0][1], pu[0][2], pu[0][3]};
-      s.part[buf][wave][1][c4] = f32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
+    if ((lane & CF::DUP) == 0) {
+      int lab = 0;
+      if constexpr (CF::NHALF >= 1) lab += (lane & CF::half_mask(0)) ? 4 : 0;
+      if constexpr (CF::NHALF >= 2) lab += (lane & CF::half_mask(1)) ? 2 : 0;
+      if constexpr (CF::NHALF >= 3) lab += (lane & CF::half_mask(2)) ? 1 : 0;
+      float* pp = reinterpret_cast<float*>(&s.part[buf][wave][lab >> 2][c4]) + (lab & 3);
+      if constexpr (CF::NOUT == 8) {
+        s.part[buf][wave][0][c4] = f32x4{acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+        s.part[buf][wave][1][c4] = f32x4{acc[0][4], acc[0][5], acc[0][6], acc[0][7]};
+      } else if constexpr (CF::NOUT == 4) {
+        *reinterpret_cast<f32x4*>(pp) = f32x4{acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+      } else if constexpr (CF::NOUT == 2) {
+        *reinterpret_cast<float2*>(pp) = make_float2(acc[0][0], acc[0][1]);
+      } else {
+        *pp = acc[0][0];
+      }
     }
     __syncthreads();
     f32x4 uu = s.part[buf][0][0][c4], ww = s.part[buf][0][1][c4];
