@@ -68,12 +68,11 @@ __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_r
 __device__ __forceinline__ float sigmoid_fast(float x) { return rcp_fast(1.0f + exp_fast(-x)); }
 __device__ __forceinline__ float silu_fast(float y) { return y * sigmoid_fast(y); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// two floats -> packed bf16 pair (round to nearest even, NaN stays NaN): v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 template <typename R> struct OutVec;
@@ -81,8 +80,8 @@ template <> struct OutVec<uint16_t> {
   // 4 bf16 outputs -> one 8-byte store
   static __device__ __forceinline__ void store(void* base, size_t idx, float a, float b, float c, float d) {
     u32x2 v;
-    v.x = bf16_rne(a) | (bf16_rne(b) << 16);
-    v.y = bf16_rne(c) | (bf16_rne(d) << 16);
+    v.x = bf16x2_rne(a, b);
+    v.y = bf16x2_rne(c, d);
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + idx) = v;
   }
 };
@@ -448,25 +447,42 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   if (!CF::PRE && tid == 0 && a.group > 1)
     prev = __hip_atomic_fetch_add(a.counters + (size_t)n * H + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---------------- phase 1a: conv + SiLU, one task per (token, staged channel)
-  for (int task = tid; task < T * NCH; task += NTHR) {
-    const int t = task / NCH, ch = task - (task / NCH) * NCH;
-    float act;
-    if constexpr (CF::PRE) {
-      act = up(s.xs[t * NCH + ch]);  // already convolved and activated
+  // ---------------- phase 1a: conv + SiLU, one task per staged channel, sliding over the
+  // tokens (taps and the three cached inputs read once per channel)
+  for (int ch = tid; ch < NCH; ch += NTHR) {
+    // destination of token t: q -> row[t][ch].y, k -> row[t][ch - K].x, v -> vs[t][ch - 2K]
+    float* dp;
+    int dstride;
+    if (ch < K) {
+      dp = reinterpret_cast<float*>(&s.row[ch]) + 1;
+      dstride = 4 * K;
+    } else if (ch < 2 * K) {
+      dp = reinterpret_cast<float*>(&s.row[ch - K]);
+      dstride = 4 * K;
     } else {
-      const float y = fmaf(up(s.ws[ch * 4 + 3]), up(ext_raw<CF, R>(s, ch, t + 3)),
-                           fmaf(up(s.ws[ch * 4 + 2]), up(ext_raw<CF, R>(s, ch, t + 2)),
-                                fmaf(up(s.ws[ch * 4 + 1]), up(ext_raw<CF, R>(s, ch, t + 1)),
-                                     up(s.ws[ch * 4 + 0]) * up(ext_raw<CF, R>(s, ch, t)))));
-      act = silu_fast(y);
+      dp = &s.vs[ch - 2 * K];
+      dstride = VT;
     }
-    if (ch < K)
-      s.row[row_slot<CF>(t, ch)].y = act;  // q, normalised in phase 2
-    else if (ch < 2 * K)
-      s.row[row_slot<CF>(t, ch - K)].x = act;  // k
-    else
-      s.vs[t * VT + (ch - 2 * K)] = act;
+    if constexpr (CF::PRE) {  // already convolved and activated
+#pragma unroll
+      for (int t = 0; t < CF::TMAX; ++t)
+        if (t < T) dp[t * dstride] = up(s.xs[t * NCH + ch]);
+    } else {
+      const float w0 = up(s.ws[ch * 4 + 0]), w1 = up(s.ws[ch * 4 + 1]);
+      const float w2 = up(s.ws[ch * 4 + 2]), w3 = up(s.ws[ch * 4 + 3]);
+      float e0 = up(s.cs[ch * 3 + 0]), e1 = up(s.cs[ch * 3 + 1]), e2 = up(s.cs[ch * 3 + 2]);
+#pragma unroll
+      for (int t = 0; t < CF::TMAX; ++t) {
+        if (t < T) {
+          const float e3 = up(s.xs[t * NCH + ch]);
+          const float y = fmaf(w3, e3, fmaf(w2, e2, fmaf(w1, e1, w0 * e0)));
+          dp[t * dstride] = silu_fast(y);
+          e0 = e1;
+          e1 = e2;
+          e2 = e3;
+        }
+      }
+    }
   }
 
   // ---------------- phase 1b: gate -> alpha, beta
@@ -545,11 +561,18 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     // per-lane partials: rows row0 + Q*r, partial m = r % M, rows of a partial in order;
     // label c is column c of u, label 4 + c column c of w
     float acc[M][8];
+    // a_i and k_i of the lane's rows, kept in registers for the update when there are few
+    constexpr bool KEEP = RPL <= 8;
+    float ra[KEEP ? RPL : 1], rk[KEEP ? RPL : 1];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       const int m = r % M;
       const f32x4 rr = rw[r * Q];
       const f32x4 sv = S[r];
+      if constexpr (KEEP) {
+        ra[r] = rr.z;
+        rk[r] = rr.w;
+      }
       if (r < M) {
         acc[m][0] = rr.x * sv.x; acc[m][1] = rr.x * sv.y; acc[m][2] = rr.x * sv.z; acc[m][3] = rr.x * sv.w;
         acc[m][4] = rr.y * sv.x; acc[m][5] = rr.y * sv.y; acc[m][6] = rr.y * sv.z; acc[m][7] = rr.y * sv.w;
@@ -608,12 +631,21 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
     float* dst = snap + ith * KV;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const f32x4 rr = rw[r * Q];
+      float al, kr;
+      if constexpr (KEEP) {
+        al = ra[r];
+        kr = rk[r];
+      } else {
+        const f32x4 rr = rw[r * Q];
+        al = rr.z;
+        kr = rr.w;
+      }
+      // a_i S_ij rounded, then + k_i d_j fused: the product lands in S's own register
       f32x4 sv = S[r];
-      sv.x = fmaf(rr.z, sv.x, rr.w * d[0]);
-      sv.y = fmaf(rr.z, sv.y, rr.w * d[1]);
-      sv.z = fmaf(rr.z, sv.z, rr.w * d[2]);
-      sv.w = fmaf(rr.z, sv.w, rr.w * d[3]);
+      sv.x = fmaf(kr, d[0], al * sv.x);
+      sv.y = fmaf(kr, d[1], al * sv.y);
+      sv.z = fmaf(kr, d[2], al * sv.z);
+      sv.w = fmaf(kr, d[3], al * sv.w);
       S[r] = sv;
       store_snapshot<CF::STP>(dst + (size_t)r * Q * V, sv);
     }
