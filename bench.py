@@ -7,7 +7,8 @@ inputs already resident in HBM. Prints one JSON line:
   value      verify tokens/s = N*T / (time per call)
   roofline   algorithmic HBM bytes per call / average kernel duration (HIP events on
              the launch stream), against the MI355X HBM peak of 8 TB/s
-  cpu_baseline  the float64 oracle on a bounded sample of the same workload, 1 core
+  cpu_baseline  the float64 oracle on bounded samples of the same workload, on all host
+                threads (sequence slices) and on one thread
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large_batch]
 """
@@ -34,15 +35,15 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, variant: str):
+def measured_traffic(workload: str, variant: str, launch: dict):
     """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source; None otherwise."""
+    the current kernel source and launch configuration; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         doc = json.load(f)
-    if doc.get("source_hash") != source_hash() or doc.get("variant") != variant:
+    if doc.get("source_hash") != source_hash() or doc.get("variant") != variant or doc.get("launch") != launch:
         return None
     return doc.get("hbm_bytes_per_call")
 
@@ -53,45 +54,86 @@ def first_sequences(inp, n):
     return {k: (v[:n].contiguous() if k in per_seq else v) for k, v in inp.items()}
 
 
-def cpu_baseline(w, inp_cpu, budget_s: float):
-    """The oracle as it is (float64, sequential C, one thread) on the first n sequences
-    of the same inputs, n chosen from a one-sequence probe to take about budget_s."""
-    import oracle
+def host_threads() -> int:
+    """Host threads for the all-core oracle leg: OMP_NUM_THREADS when set, else the CPU
+    count, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(16, n))
 
+
+def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
+    """The oracle as it is (float64, sequential C) on bounded samples of the same inputs,
+    run on slices of 4 sequences: (1) on one host thread over the first n sequences, n
+    chosen from a one-slice probe to take about budget_s / 2; (2) on all `threads` host
+    threads, each running the oracle on its own slices (ctypes releases the GIL), over as
+    many of the batch's sequences as fit in about budget_s / 2 (short samples repeated)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
     oracle.load()
+    chunk = 4
+    per_seq = ("mixed_qkv", "conv_state", "gate", "beta", "state")
+
+    def run_slice(ab):
+        a, b = ab
+        part = {k: (v[a:b].contiguous() if k in per_seq else v) for k, v in inp_cpu.items()}
+        oracle.verify_workload(w.with_(N=b - a), part)
+        return b - a
+
+    def slices(n, passes=1):
+        return [(a, min(a + chunk, n)) for a in range(0, n, chunk)] * passes
+
     t0 = time.perf_counter()
-    oracle.verify_workload(w.with_(N=1), first_sequences(inp_cpu, 1))
-    t1 = time.perf_counter() - t0
-    n = int(max(1, min(w.N, budget_s / max(t1, 1e-6))))
-    sample = first_sequences(inp_cpu, n)
+    run_slice((0, min(chunk, w.N)))
+    probe = (time.perf_counter() - t0) / min(chunk, w.N)  # seconds per sequence
+    n = int(max(1, min(w.N, 0.5 * budget_s / max(probe, 1e-6))))
+    passes1 = int(max(1, min(20, round(0.5 * budget_s / max(n * probe, 1e-6)))))
     t0 = time.perf_counter()
-    oracle.verify_workload(w.with_(N=n), sample)
+    done1 = sum(run_slice(ab) for ab in slices(n, passes1))
     el = time.perf_counter() - t0
-    return {
-        "value": n * w.T / el,
-        "unit": "tokens/s",
-        "cores": 1,
-        "kind": "oracle",
+    single = {
+        "value": done1 * w.T / el, "unit": "tokens/s", "cores": 1,
         "sample": f"first {n} of {w.N} sequences ({n * w.HV} of {w.units} (sequence, value-head) units), "
-                  f"all T={w.T} tokens, same inputs; {el:.1f} s on one host thread",
+                  f"all T={w.T} tokens, {passes1} pass(es), slices of {chunk} sequences; {el:.1f} s on one "
+                  f"host thread",
+    }
+
+    seq_rate = threads * done1 / max(el, 1e-6)  # expected sequences/s on all threads
+    n_mt = int(min(w.N, max(threads * chunk, 0.5 * budget_s * seq_rate)))
+    passes = int(max(1, min(20, round(0.5 * budget_s * seq_rate / n_mt))))
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        done = sum(ex.map(run_slice, slices(n_mt, passes)))
+        el_mt = time.perf_counter() - t0
+    return {
+        "value": done * w.T / el_mt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {n_mt} of {w.N} sequences ({n_mt * w.HV} of {w.units} (sequence, value-head) units), "
+                  f"all T={w.T} tokens, same inputs, {passes} pass(es), in slices of {chunk} sequences over "
+                  f"{threads} host threads; {el_mt:.1f} s",
+        "single_thread": single,
     }
 
 
-def sweep(out_path: str, quick: bool = False) -> None:
-    """H = HV x T x N sweep over every tile width and snapshot store policy (K = V = 128,
-    bf16, softplus). Buffer sets are rotated so that at least 1 GiB is touched between
-    reuses (small shapes would otherwise run from the 256 MB last-level cache). Writes one
-    JSON object per shape to out_path and prints a summary table."""
+def sweep(out_path: str, quick: bool = False, hs=None) -> None:
+    """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
+    cap (K = V = 128, bf16, softplus). Buffer sets are rotated so that at least 1 GiB is
+    touched between reuses (small shapes would otherwise run from the 256 MB last-level
+    cache). A cap is timed only where the grid has more workgroups than the cap lets run at
+    once. Writes one JSON object per shape to out_path and prints a summary line."""
     import torch
 
     import linear_attention_decode_kda_amd as kda
     from linear_attention_decode_kda_amd import synth
 
     dev = torch.device("cuda:0")
-    Hs = (8, 32) if quick else (8, 16, 32, 64)
+    Hs = tuple(hs) if hs else (8, 32) if quick else (8, 16, 32, 64)
     Ts = (2, 4, 8) if quick else (1, 2, 4, 6, 8)
     Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
-    combos = [(t, pol) for t in (32, 64, 128) for pol in (1, 2)]
+    combos = [(t, pol, occ) for t in (32, 64, 128) for pol in (1, 2) for occ in (0, 6, 4, 2, 1)]
     rows = []
     with open(out_path, "w") as f:
         for H in Hs:
@@ -115,21 +157,24 @@ def sweep(out_path: str, quick: bool = False) -> None:
                         }
                         sets.append((inp, kda.alloc_outputs(w, dev)))
                     res = {}
-                    for tile, pol in combos + [(0, 0)]:
-                        p = kda.params_for(w, tile_columns=tile, store_policy=pol)
+                    for tile, pol, occ in combos + [(0, 0, 0)]:
+                        if occ and N * H * (128 // tile) <= 256 * occ:
+                            continue  # the cap would not bind
+                        p = kda.params_for(w, tile_columns=tile, store_policy=pol, max_wg_per_cu=occ)
                         ws = kda.alloc_workspace(p, dev)
+                        calls = [kda.PreparedVerify(p, a, o, ws) for a, o in sets]
                         for i in range(2 * nset):
-                            kda.run(p, sets[i % nset][0], sets[i % nset][1], ws)
+                            calls[i % nset]()
                         reps = max(8, 2 * nset)
                         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                               for _ in range(reps)]
                         for i in range(reps):
                             ev[i][0].record()
-                            kda.run(p, sets[i % nset][0], sets[i % nset][1], ws)
+                            calls[i % nset]()
                             ev[i][1].record()
                         torch.cuda.synchronize()
                         ms = sorted(a.elapsed_time(b) for a, b in ev)
-                        res[f"{tile}/{pol}" if tile else "auto"] = ms[len(ms) // 2]
+                        res[(f"{tile}/{pol}" + (f"/{occ}" if occ else "")) if tile else "auto"] = ms[len(ms) // 2]
                     best = min((v, k) for k, v in res.items() if k != "auto")
                     auto_p = kda.params_for(w)
                     row = {"H": H, "T": T, "N": N, "units": N * H, "bytes": b_alg, "ms": res,
@@ -162,11 +207,13 @@ def main():
                          "step, or the unfused two-kernel form of verify (same algorithmic bytes)")
     ap.add_argument("--tile", type=int, default=0, help="override: V columns per workgroup (32, 64, 128)")
     ap.add_argument("--store", type=int, default=0, help="override: snapshot stores, 1 streaming, 2 write-through")
+    ap.add_argument("--occ", type=int, default=0, help="override: at most 1, 2, 4 or 6 workgroups per CU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
                     help="run the H x T x N sweep over tile widths and store policies instead")
     ap.add_argument("--sweep-quick", action="store_true", help="a reduced sweep grid")
+    ap.add_argument("--sweep-h", default="", help="comma-separated H = HV values for --sweep (default all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -185,7 +232,7 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.sweep:
-        sweep(args.sweep, args.sweep_quick)
+        sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x])
         return
 
     if args.copy_calibration:
@@ -200,7 +247,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     variant = {"auto": kda.VARIANT_AUTO, "small": kda.VARIANT_SMALL, "large": kda.VARIANT_LARGE}[args.variant]
-    p = kda.params_for(w, variant=variant, tile_columns=args.tile, store_policy=args.store)
+    p = kda.params_for(w, variant=variant, tile_columns=args.tile, store_policy=args.store,
+                       max_wg_per_cu=args.occ)
     resolved = {kda.VARIANT_SMALL: "small", kda.VARIANT_LARGE: "large"}[kda.select_variant(p)]
     print(f"[bench] workload={w.name} N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V} "
           f"{w.dtype} {w.gate} variant={resolved}", file=sys.stderr, flush=True)
@@ -210,10 +258,20 @@ def main():
     ws = kda.alloc_workspace(p, dev)
     stream = torch.cuda.current_stream()
 
+    nset = 1
     if args.op == "verify":
-        def step():
-            kda.run(p, inp, out, ws, stream)
+        # Rotate distinct buffer sets so that >= 1 GiB is touched between reuses: a workload
+        # smaller than that would otherwise run partly from the 256 MB last-level cache.
         b_alg = synth.algorithmic_bytes(w)
+        nset = max(1, min(8, -(-(1 << 30) // b_alg)))
+        sets = [(inp, out)] + [({k: v.clone() for k, v in inp.items()}, kda.alloc_outputs(w, dev))
+                               for _ in range(nset - 1)]
+        calls = [kda.PreparedVerify(p, a, o, ws, stream) for a, o in sets]  # checks once; one C call each
+        rot = [0]
+
+        def step():
+            calls[rot[0] % nset]()
+            rot[0] += 1
     elif args.op == "unfused":
         act = torch.empty((w.N, w.T, w.C), dtype=torch.float32, device=dev)
 
@@ -286,11 +344,12 @@ def main():
           f"{achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}",
           file=sys.stderr, flush=True)
 
-    traffic = measured_traffic(w.name, resolved) if args.op == "verify" else None
+    launch = kda.select_launch(p)
+    traffic = measured_traffic(w.name, resolved, launch) if args.op == "verify" else None
     cpu = None
     if not args.no_cpu_baseline and args.op == "verify":
         print("[bench] timing the float64 oracle on a bounded sample (cpu_baseline)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, inp_cpu, args.cpu_budget)
+        cpu = cpu_baseline(w, inp_cpu, args.cpu_budget, host_threads())
 
     line = {
         "metric": "verify tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
@@ -310,8 +369,8 @@ def main():
             "workload": f"{w.name}: N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V}",
             "op": args.op,
             "N": w.N, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V,
-            "in_dtype": w.dtype, "state_dtype": "f32", "gate": w.gate, "variant": resolved,
-            "algorithmic_bytes_per_call": b_alg,
+            "in_dtype": w.dtype, "state_dtype": "f32", "gate": w.gate, "variant": resolved, "launch": launch,
+            "algorithmic_bytes_per_call": b_alg, "buffer_sets": nset,
             "hbm_gbps": achieved, "pct_of_hbm_peak": 100 * achieved / HBM_PEAK_GBPS,
         },
         "roofline": {

@@ -86,6 +86,9 @@ typedef struct {
                                V selects LARGE, fewer SMALL, and overrides `variant` */
   int32_t store_policy;     /* snapshot stores: 1 streaming (non-temporal), 2 write-through
                                at device scope */
+  int32_t max_wg_per_cu;    /* at most 1, 2, 4 or 6 workgroups per compute unit, by reserving
+                               LDS per workgroup (fewer concurrent snapshot streams can use
+                               HBM better); the kernel's own limits still apply */
 } kda_verify_params;
 
 #define KDA_MAX_T 16
@@ -110,6 +113,13 @@ kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream
 /* The variant AUTO resolves to for these params (host-only, no HIP call), or a
  * negative kda_status for invalid params. */
 int32_t kda_select_variant(const kda_verify_params* p);
+
+/* The launch configuration kda_conv_verify_decode would use for these params (after the
+ * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 write-through)
+ * and workgroups-per-CU cap (0 = none). Host-only; any output pointer may be NULL.
+ * Returns the params' validation status (outputs untouched unless KDA_OK). */
+kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
+                             int32_t* max_wg_per_cu);
 
 /* Validate params and pointers without launching (host-only, no HIP call). */
 kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,

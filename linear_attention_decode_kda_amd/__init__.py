@@ -43,6 +43,7 @@ class Params(ctypes.Structure):
         ("lower_bound", ctypes.c_float), ("softplus_beta", ctypes.c_float),
         ("softplus_threshold", ctypes.c_float), ("scale", ctypes.c_float), ("l2norm_eps", ctypes.c_float),
         ("tile_columns", ctypes.c_int32), ("store_policy", ctypes.c_int32),
+        ("max_wg_per_cu", ctypes.c_int32),
     ]
 
 
@@ -84,6 +85,9 @@ def load() -> ctypes.CDLL:
     lib.kda_workspace_reset.restype = ctypes.c_int
     lib.kda_select_variant.argtypes = [PP]
     lib.kda_select_variant.restype = ctypes.c_int32
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    lib.kda_select_launch.argtypes = [PP, I32P, I32P, I32P]
+    lib.kda_select_launch.restype = ctypes.c_int
     lib.kda_validate.argtypes = [PP] + [_VP] * 12 + [_SZ]
     lib.kda_validate.restype = ctypes.c_int
     lib.kda_conv_verify_decode.argtypes = [PP] + [_VP] * 12 + [_SZ, _VP]
@@ -111,7 +115,8 @@ def lib_status_string(status: int) -> str:
 def make_params(N: int, T: int, H: int, HV: int, K: int, V: int, *, dtype: str = "bf16",
                 gate: str = "softplus", variant: int = VARIANT_AUTO, lower_bound: float = -5.0,
                 softplus_beta: float = 1.0, softplus_threshold: float = 20.0, scale: float = 0.0,
-                l2norm_eps: float = 1e-6, tile_columns: int = 0, store_policy: int = 0) -> Params:
+                l2norm_eps: float = 1e-6, tile_columns: int = 0, store_policy: int = 0,
+                max_wg_per_cu: int = 0) -> Params:
     p = Params()
     load().kda_verify_params_init(ctypes.byref(p), N, T, H, HV, K, V)
     p.in_dtype = {"f32": F32, "bf16": BF16}[dtype]
@@ -124,6 +129,7 @@ def make_params(N: int, T: int, H: int, HV: int, K: int, V: int, *, dtype: str =
     p.l2norm_eps = l2norm_eps
     p.tile_columns = tile_columns
     p.store_policy = store_policy
+    p.max_wg_per_cu = max_wg_per_cu
     return p
 
 
@@ -138,6 +144,16 @@ def workspace_bytes(p: Params) -> int:
 
 def select_variant(p: Params) -> int:
     return int(load().kda_select_variant(ctypes.byref(p)))
+
+
+def select_launch(p: Params) -> Dict[str, int]:
+    """The launch configuration the library picks for ``p``: tile_columns, store_policy
+    (1 streaming, 2 write-through) and max_wg_per_cu (0 = no cap)."""
+    t, s, o = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = load().kda_select_launch(ctypes.byref(p), ctypes.byref(t), ctypes.byref(s), ctypes.byref(o))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_select_launch")
+    return {"tile_columns": t.value, "store_policy": s.value, "max_wg_per_cu": o.value}
 
 
 def _stream(stream) -> int:
@@ -165,9 +181,9 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 def _check(name, t: torch.Tensor, shape, dtype):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
@@ -175,13 +191,9 @@ def _check(name, t: torch.Tensor, shape, dtype):
         raise ValueError(f"{name} must be contiguous")
 
 
-def kda_conv_verify_decode(p: Params, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
-                           o, inter_ssm, conv_window, workspace, stream=None) -> None:
-    """One fused verify step on the current (or given) stream; see include/kda_verify.h.
-
-    Writes o, inter_ssm, conv_window, and conv_state in place. Raises KdaError on a
-    non-OK status (nothing was launched in that case).
-    """
+def _verify_args(p: Params, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
+                 o, inter_ssm, conv_window, workspace):
+    """Check the tensors of a verify call against ``p``; returns their 12 device pointers."""
     N, T, H, HV, K, V = p.N, p.T, p.H, p.HV, p.K, p.V
     C = 2 * H * K + HV * V
     dt = _TORCH_DT.get(p.in_dtype)
@@ -198,12 +210,49 @@ def kda_conv_verify_decode(p: Params, mixed_qkv, conv_weight, conv_state, gate, 
     _check("o", o, (N, T, HV, V), dt)
     _check("inter_ssm", inter_ssm, (N, T, HV, K, V), torch.float32)
     _check("conv_window", conv_window, (N, T, C, 3), dt)
-    ptrs = [t.data_ptr() for t in (mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    return [t.data_ptr() for t in (mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
                                    o, inter_ssm, conv_window, workspace)]
-    st = load().kda_conv_verify_decode(ctypes.byref(p), *[_VP(x) for x in ptrs],
-                                       workspace.numel() * workspace.element_size(), _VP(_stream(stream)))
+
+
+def kda_conv_verify_decode(p: Params, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
+                           o, inter_ssm, conv_window, workspace, stream=None) -> None:
+    """One fused verify step on the current (or given) stream; see include/kda_verify.h.
+
+    Writes o, inter_ssm, conv_window, and conv_state in place. Raises KdaError on a
+    non-OK status (nothing was launched in that case).
+    """
+    ptrs = _verify_args(p, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state,
+                        o, inter_ssm, conv_window, workspace)
+    st = load().kda_conv_verify_decode(ctypes.byref(p), *ptrs, workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
     if st != KDA_OK:
         raise KdaError(st, "kda_conv_verify_decode")
+
+
+class PreparedVerify:
+    """``kda_conv_verify_decode`` bound to fixed tensors and a stream, for loops that reuse
+    their buffers (a serving step, a benchmark): the argument checks run once, here, and
+    each call is a single C call with the cached pointers. The caller keeps the tensors'
+    storage in place while the object is used (it holds references, so they stay alive)."""
+
+    def __init__(self, p: Params, inp: Dict[str, torch.Tensor], out: Dict[str, torch.Tensor],
+                 workspace: torch.Tensor, stream=None):
+        tensors = (inp["mixed_qkv"], inp["conv_weight"], inp["conv_state"], inp["gate"], inp["A_log"],
+                   inp["dt_bias"], inp["beta"], inp["state"], out["o"], out["inter_ssm"], out["conv_window"],
+                   workspace)
+        ptrs = _verify_args(p, *tensors)
+        self.params = Params.from_buffer_copy(p)
+        self._keep = tensors
+        self._fn = load().kda_conv_verify_decode
+        self._args = (ctypes.byref(self.params), *ptrs, workspace.numel() * workspace.element_size(),
+                      _stream(stream))
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != KDA_OK:
+            raise KdaError(st, "kda_conv_verify_decode")
 
 
 def _index(name, t, N):

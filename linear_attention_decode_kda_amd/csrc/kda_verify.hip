@@ -811,40 +811,70 @@ __global__ void zero_words(uint32_t* p, size_t n) {
 // ----------------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------------
-using LaunchFn = hipError_t (*)(const Args&, hipStream_t);
+using LaunchFn = hipError_t (*)(const Args&, int, hipStream_t);
+
+// LDS a workgroup reserves so that at most `wg_per_cu` of them share a CU (0: no cap
+// beyond the kernel's own LDS and VGPRs). The reservation is dynamic LDS on top of the
+// kernel's static record; the kernel never touches it. Sizes from MI355X measurements
+// (rocprofv3 MeanOccupancyPerCU and timings): workgroups holding 98 KiB run one per CU,
+// 53 KiB two, 35.5 KiB four, 23.5 KiB six.
+size_t lds_reservation(int wg_per_cu) {
+  switch (wg_per_cu) {
+    case 1: return 100352;
+    case 2: return 54272;
+    case 4: return 36352;
+    case 6: return 24064;
+    default: return 0;
+  }
+}
 
 template <class CF, typename R>
-hipError_t launch(const Args& a, hipStream_t stream) {
+hipError_t launch(const Args& a, int wg_per_cu, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.N * a.HV * CF::NVT);
   Args copy = a;
   copy.group = a.g * CF::NVT;
   void* args[] = {&copy};
+  const size_t want = lds_reservation(wg_per_cu), have = sizeof(Smem<CF, R>);
   return hipLaunchKernel(reinterpret_cast<const void*>(&kda_verify_kernel<CF, R>), dim3(grid),
-                         dim3(CF::NTHR), args, 0, stream);
+                         dim3(CF::NTHR), args, want > have ? want - have : 0, stream);
 }
 
-// Tile shape and store policy, from an H = HV x T x N sweep on MI355X (K = V = 128, bf16,
-// every tile width and store policy timed on each shape, buffers rotated so that each
-// run reads and writes HBM):
-//   <= 128 (sequence, value head) units: the 32-column split (4 WGs per unit): a latency-
-//     bound grid, where a quarter of the per-token work per WG shortens the critical path
-//     (graph-replayed: 10.7 vs 15.1 us at N = 1, HV = 8, T = 4);
-//   up to 4096 units: the whole-V tile; write-through stores from T = 4;
-//   >= 4096 units: whole V at T <= 2, the 32-column split at T <= 6 (shorter WGs trim the
-//     tail of the grid), whole V with write-through stores at T >= 8.
+// Tile shape, store policy and workgroups-per-CU cap, from an H = HV x T x N sweep on
+// MI355X (K = V = 128, bf16; every tile width, store policy and cap timed on each shape,
+// buffers rotated so that each run reads and writes HBM; the choice per (T, units) bucket
+// is the one with the best mean over H). A cap limits how many workgroups stream
+// snapshots at once; from about a thousand units up, fewer concurrent streams keep HBM
+// busier (one whole-V workgroup per CU reaches 74-77 % of peak at T >= 6, against
+// 66-69 % uncapped).
+//   <= 128 units: the 32-column split (4 WGs per unit): a latency-bound grid, where a
+//     quarter of the per-token work per WG shortens the critical path;
+//   T <= 2: whole V, two WGs per CU from 1024 units;
+//   T <= 5: 64 columns below 512 units, whole V below 1024, whole V with two WGs per CU
+//     below 2048, 32 columns with four WGs per CU below 8192, then whole V, one per CU;
+//   T >= 6: 64 columns below 512 units, 64 columns two per CU below 1024, whole V with
+//     write-through stores two per CU below 2048, then whole V, one per CU.
 // Every tile width uses the same K split (32 rows per wave) and the same partial-sum tree,
-// so all of them return bit-identical results.
+// so all of them return bit-identical results; the cap only changes scheduling.
 struct Tile {
-  int vt;   // V columns per WG
-  int stp;  // StorePolicy
+  int vt;       // V columns per WG
+  int stp;      // StorePolicy
+  int occ = 0;  // workgroups per CU cap (lds_reservation), 0 = none
 };
 
 Tile auto_tile_128(long long units, int T) {
   if (units <= 128) return Tile{32, kStoreNT};
-  if (units < 4096) return Tile{128, T >= 4 ? kStoreSC1 : kStoreNT};
-  if (T <= 2) return Tile{128, kStoreNT};
-  if (T <= 6) return Tile{32, kStoreNT};
-  return Tile{128, kStoreSC1};
+  if (T <= 2) return units < 1024 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 2};
+  if (T <= 5) {
+    if (units < 512) return Tile{64, kStoreNT};
+    if (units < 1024) return Tile{128, kStoreNT};
+    if (units < 2048) return Tile{128, kStoreNT, 2};
+    if (units < 8192) return Tile{32, kStoreNT, 4};
+    return Tile{128, kStoreNT, 1};
+  }
+  if (units < 512) return Tile{64, kStoreNT};
+  if (units < 1024) return Tile{64, kStoreNT, 2};
+  if (units < 2048) return Tile{128, kStoreSC1, 2};
+  return Tile{128, kStoreNT, 1};
 }
 
 Tile choose_tile(const kda_verify_params* p) {
@@ -858,6 +888,7 @@ Tile choose_tile(const kda_verify_params* p) {
     else if (p->variant == KDA_VARIANT_SMALL)
       t.vt = 32;
     if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreSC1 : kStoreNT;
+    if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu;
     return t;
   }
   if (K == 64 && V == 64) return {p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT};
@@ -932,6 +963,7 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
   p->l2norm_eps = 1e-6f;
   p->tile_columns = 0;
   p->store_policy = 0;
+  p->max_wg_per_cu = 0;
 }
 
 static kda_status check_params(const kda_verify_params* p) {
@@ -949,6 +981,9 @@ static kda_status check_params(const kda_verify_params* p) {
   if (p->variant < KDA_VARIANT_AUTO || p->variant > KDA_VARIANT_LARGE) return KDA_ERR_UNSUPPORTED;
   if (!(p->softplus_beta > 0.0f) || !(p->l2norm_eps >= 0.0f) || p->scale != p->scale) return KDA_ERR_SHAPE;
   if (p->store_policy < 0 || p->store_policy > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->max_wg_per_cu != 0 && p->max_wg_per_cu != 1 && p->max_wg_per_cu != 2 && p->max_wg_per_cu != 4 &&
+      p->max_wg_per_cu != 6)
+    return KDA_ERR_UNSUPPORTED;
   if (p->tile_columns != 0) {
     const bool ok = p->K == 128 && p->V == 128 &&
                     (p->tile_columns == 32 || p->tile_columns == 64 || p->tile_columns == 128);
@@ -970,6 +1005,17 @@ int32_t kda_select_variant(const kda_verify_params* p) {
   if (p->tile_columns != 0) return p->tile_columns == p->V ? KDA_VARIANT_LARGE : KDA_VARIANT_SMALL;
   if (p->variant != KDA_VARIANT_AUTO) return p->variant;
   return choose_tile(p).vt < p->V ? KDA_VARIANT_SMALL : KDA_VARIANT_LARGE;
+}
+
+kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
+                             int32_t* max_wg_per_cu) {
+  const kda_status st = check_params(p);
+  if (st != KDA_OK) return st;
+  const Tile t = choose_tile(p);
+  if (tile_columns) *tile_columns = t.vt;
+  if (store_policy) *store_policy = t.stp == kStoreSC1 ? 2 : 1;
+  if (max_wg_per_cu) *max_wg_per_cu = t.occ;
+  return KDA_OK;
 }
 
 }  // extern "C"
@@ -1099,7 +1145,8 @@ kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const v
                          const void* conv_weight, void* conv_state, const void* gate, const float* A_log,
                          const float* dt_bias, const void* beta, const float* state, void* o, float* inter_ssm,
                          void* conv_window, void* workspace, hipStream_t stream, bool pre) {
-  LaunchFn fn = pick_launch(p, choose_tile(p), pre);
+  const Tile tl = choose_tile(p);
+  LaunchFn fn = pick_launch(p, tl, pre);
   if (!fn) return KDA_ERR_UNSUPPORTED;
   Args a;
   a.mixed_qkv = mixed_qkv;
@@ -1133,7 +1180,7 @@ kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const v
   a.softplus_threshold = p->softplus_threshold;
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->K);
   a.eps = p->l2norm_eps;
-  return fn(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  return fn(a, tl.occ, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 }  // namespace kda

@@ -50,6 +50,7 @@ def stats(csv_path: str, cmd: str, out: str) -> None:
 def traffic(workload, variant, fetch, write, cfetch, cwrite, cmd_file, out) -> None:
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     from bench import source_hash  # the same hash bench.py checks
+    import linear_attention_decode_kda_amd as kda
     from linear_attention_decode_kda_amd import synth
 
     kf, nf = _counter(fetch, "FETCH_SIZE", KERNEL_TAG)
@@ -66,6 +67,7 @@ def traffic(workload, variant, fetch, write, cfetch, cwrite, cmd_file, out) -> N
     doc = {
         "workload": workload,
         "variant": variant,
+        "launch": kda.select_launch(kda.params_for(synth.WORKLOADS[workload])),
         "source_hash": source_hash(),
         "commands": cmds,
         "kernel_fetch_kib_per_dispatch": kf,

@@ -53,10 +53,10 @@ def test_workspace_bytes(lib):
 
 
 def test_select_variant(lib):
-    assert kda.select_variant(kda.make_params(256, 4, 32, 32, 128, 128)) == kda.VARIANT_SMALL
+    assert kda.select_variant(kda.make_params(256, 4, 32, 32, 128, 128)) == kda.VARIANT_LARGE
     assert kda.select_variant(kda.make_params(32, 4, 16, 16, 128, 128)) == kda.VARIANT_LARGE
     assert kda.select_variant(kda.make_params(4, 8, 16, 16, 128, 128)) == kda.VARIANT_SMALL
-    assert kda.select_variant(kda.make_params(64, 3, 16, 32, 128, 128)) == kda.VARIANT_LARGE
+    assert kda.select_variant(kda.make_params(64, 3, 16, 32, 128, 128)) == kda.VARIANT_SMALL
     assert kda.select_variant(kda.make_params(512, 8, 16, 64, 128, 128)) == kda.VARIANT_LARGE
     assert kda.select_variant(kda.make_params(2, 2, 2, 2, 16, 16)) == kda.VARIANT_LARGE
     for v in (kda.VARIANT_SMALL, kda.VARIANT_LARGE):
@@ -203,10 +203,52 @@ def test_tuning_overrides(lib):
     assert kda.select_variant(p) == kda.VARIANT_LARGE
     p = kda.make_params(8, 4, 2, 2, 128, 128, tile_columns=32, variant=kda.VARIANT_LARGE)
     assert kda.select_variant(p) == kda.VARIANT_SMALL  # the tile override wins
-    for bad in (dict(tile_columns=48), dict(store_policy=3)):
+    for bad in (dict(tile_columns=48), dict(store_policy=3), dict(max_wg_per_cu=3), dict(max_wg_per_cu=8),
+                dict(max_wg_per_cu=-1)):
         p = kda.make_params(8, 4, 2, 2, 128, 128, **bad)
         ptrs, wsb = _fake_ptrs(p)
         assert _validate(lib, p, ptrs, wsb) == -3
+    for good in (1, 2, 4, 6):
+        p = kda.make_params(8, 4, 2, 2, 128, 128, max_wg_per_cu=good)
+        ptrs, wsb = _fake_ptrs(p)
+        assert _validate(lib, p, ptrs, wsb) == 0
     p = kda.make_params(8, 4, 2, 2, 64, 64, tile_columns=64)  # overrides exist for K = V = 128 only
     ptrs, wsb = _fake_ptrs(p)
     assert _validate(lib, p, ptrs, wsb) == -3
+
+
+def test_prepared_call_checks_arguments_once():
+    """PreparedVerify runs the same argument checks as the plain call (no GPU needed to
+    see a rejection: CPU tensors are refused before anything reaches the library)."""
+    import torch
+    from linear_attention_decode_kda_amd import synth
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w)
+    out = {"o": torch.empty(w.N, w.T, w.HV, w.V), "inter_ssm": torch.empty(w.N, w.T, w.HV, w.K, w.V),
+           "conv_window": torch.empty(w.N, w.T, w.C, 3)}
+    p = kda.params_for(w)
+    with pytest.raises(ValueError, match="GPU device"):
+        kda.PreparedVerify(p, inp, out, torch.zeros(256, dtype=torch.uint8))
+
+
+def test_select_launch_follows_the_dispatch_rule(lib):
+    """The AUTO rule (tile, stores, workgroups-per-CU cap) on the named workloads and at
+    the edges of its buckets, and the overrides winning over it."""
+    L = lambda *shape, **kw: tuple(kda.select_launch(kda.make_params(*shape, **kw)).values())
+    assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0)            # tiny: the only K = V = 16 tile
+    assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0)       # small batch: 512 units, T = 4
+    assert L(64, 3, 16, 32, 128, 128) == (32, 1, 4)        # GVA: 2048 units, T = 3
+    assert L(256, 4, 32, 32, 128, 128) == (128, 1, 1)      # large batch: 8192 units
+    assert L(512, 8, 16, 64, 128, 128) == (128, 1, 1)      # max bandwidth: 32768 units, T = 8
+    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0)           # <= 128 units: latency-bound split
+    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0)        # T <= 2 below 1024 units
+    assert L(32, 2, 32, 32, 128, 128) == (128, 1, 2)
+    assert L(8, 4, 32, 32, 128, 128) == (64, 1, 0)         # T <= 5
+    assert L(32, 4, 32, 32, 128, 128) == (128, 1, 2)
+    assert L(8, 6, 32, 32, 128, 128) == (64, 1, 0)         # T >= 6
+    assert L(16, 6, 32, 32, 128, 128) == (64, 1, 2)
+    assert L(32, 8, 32, 32, 128, 128) == (128, 2, 2)
+    assert L(64, 8, 32, 32, 128, 128) == (128, 1, 1)
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6)
+    assert kda.make_params(1, 0, 1, 1, 128, 128) and lib.kda_select_launch(
+        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None) == -2

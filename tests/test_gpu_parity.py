@@ -248,14 +248,16 @@ def test_every_tile_shape_bit_identical(w):
 
 
 def test_explicit_tile_and_store_overrides_bit_identical():
-    """Every tile width (32, 64, 128 columns per WG) and both snapshot store policies give
-    the same bits; one of them is checked against the oracle."""
+    """Every tile width (32, 64, 128 columns per WG), both snapshot store policies and the
+    workgroups-per-CU caps give the same bits; one of them is checked against the oracle."""
     w = W(5, 3, 2, 4, 128, 128, gate="safe")
     inp = synth.make_inputs(w)
     outs = []
     for tile in (32, 64, 128):
         for pol in (1, 2):
             outs.append(run_gpu(w, inp, A, tile_columns=tile, store_policy=pol))
+    for tile, occ in ((32, 1), (64, 2), (128, 4), (64, 6), (128, 1)):  # per-CU caps: scheduling only
+        outs.append(run_gpu(w, inp, A, tile_columns=tile, max_wg_per_cu=occ))
     for o in outs[1:]:
         for k in ("o", "inter_ssm", "conv_window", "conv_state"):
             assert torch.equal(o[k], outs[0][k]), k

@@ -218,3 +218,26 @@ def test_graph_replay_matches_eager():
             assert torch.equal(out[k], eager[k]), (rep, k)
         assert torch.equal(g["conv_state"], eager_cs), rep
     assert_matches(w, {**eager, "conv_state": eager_cs}, oracle.verify_workload(w, inp), what="graph")
+
+
+def test_prepared_call_matches_plain_call():
+    """PreparedVerify (checks once, cached pointers) returns the same bits as the plain
+    call, call after call on a chain of rolled conv caches, and matches the oracle."""
+    w = synth.WORKLOADS["gva"].with_(N=8)
+    say("[gpu] prepared call vs plain call, gva N=8, 3 chained calls")
+    inp, g, p, ws, out = _setup(w)
+    g2 = {k: v.clone() for k, v in g.items()}
+    out2 = kda.alloc_outputs(w)
+    ws2 = kda.alloc_workspace(p)
+    call = kda.PreparedVerify(p, g2, out2, ws2)
+    for i in range(3):
+        kda.run(p, g, out, ws)
+        call()
+        torch.cuda.synchronize()
+        for k in out:
+            assert torch.equal(out[k].view(torch.int16 if out[k].element_size() == 2 else torch.int32),
+                               out2[k].view(torch.int16 if out2[k].element_size() == 2 else torch.int32)), (i, k)
+        assert torch.equal(g["conv_state"].view(torch.int16), g2["conv_state"].view(torch.int16)), i
+        if i == 0:
+            assert_matches(w, {**out2, "conv_state": g2["conv_state"]}, oracle.verify_workload(w, inp),
+                           what="prepared")
