@@ -3,6 +3,7 @@
   python -m linear_attention_decode_kda_amd.rocprof_summary stats <kernel_stats.csv> <cmd> <out.md>
   python -m linear_attention_decode_kda_amd.rocprof_summary traffic <workload> <variant>
          <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <cmd-file> <out.json>
+  python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md <sweep.jsonl> <cmd> <out.md>
 
 `traffic` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the verify
 kernel by what the same counters read for a plain 1 GiB device copy (read 1 GiB, write
@@ -88,10 +89,47 @@ def traffic(workload, variant, fetch, write, cfetch, cwrite, cmd_file, out) -> N
         f.write("\n")
 
 
+def sweep_md(jsonl: str, cmd: str, out: str) -> None:
+    """Table of a `bench.py --sweep` run: per shape the best (tile/store[/cap]) and its
+    share of the HBM peak, the AUTO choice and its share, and three reference launches."""
+    import linear_attention_decode_kda_amd as kda
+
+    rows = [json.loads(ln) for ln in open(jsonl) if ln.strip()]
+    pct = lambda r, k: 100.0 * r["bytes"] / r["ms"][k] / 1e6 / 8000.0 if k in r["ms"] else float("nan")
+    refs = ("32/1", "128/1", "128/1/1")
+    lines = ["# H = HV x T x N sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
+             f"Command: `{cmd}` (one MI355X; each shape's buffers rotated so that >= 1 GiB is touched "
+             "between reuses; median of >= 8 calls per combination), summarised by "
+             f"`python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md {os.path.basename(jsonl)} ...`.",
+             "",
+             "Combinations are tile/store[/cap]: V columns per workgroup, snapshot stores (1 streaming, "
+             "2 write-through), and the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed only "
+             "where the grid has more workgroups than it lets run at once). Percent of the 8 TB/s HBM "
+             "peak = algorithmic bytes / kernel time. Shapes of <= 128 units are launch-latency-bound: "
+             "their timings include the launch, and the columns differ by noise.", "",
+             "| H=HV | T | N | units | best | best % | AUTO | AUTO % | AUTO/best | " + " | ".join(refs) + " |",
+             "|---|---|---|---|---|---|---|---|---|" + "---|" * len(refs)]
+    for r in rows:
+        p = kda.make_params(r["N"], r["T"], r["H"], r["H"], 128, 128)
+        ln = kda.select_launch(p)
+        auto = f"{ln['tile_columns']}/{ln['store_policy']}" + (f"/{ln['max_wg_per_cu']}" if ln["max_wg_per_cu"] else "")
+        lines.append(f"| {r['H']} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | {r['best_pct']:.1f} | {auto} | "
+                     f"{pct(r, 'auto'):.1f} | {r['auto_over_best']:.3f} | "
+                     + " | ".join(f"{pct(r, k):.1f}" if k in r["ms"] else "-" for k in refs) + " |")
+    mean = statistics.mean(r["auto_over_best"] for r in rows)
+    big = [r for r in rows if r["units"] >= 256]
+    lines += ["", f"AUTO over best, mean over all {len(rows)} shapes: {mean:.3f}; over the {len(big)} shapes "
+              f"of >= 256 units: {statistics.mean(r['auto_over_best'] for r in big):.3f}."]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(*sys.argv[2:5])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10])
+    elif sys.argv[1] == "sweep-md":
+        sweep_md(*sys.argv[2:5])
     else:
         raise SystemExit(__doc__)
