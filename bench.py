@@ -133,7 +133,7 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
     Hs = tuple(hs) if hs else (8, 32) if quick else (8, 16, 32, 64)
     Ts = (2, 4, 8) if quick else (1, 2, 4, 6, 8)
     Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
-    combos = [(t, pol, occ) for t in (32, 64, 128) for pol in (1, 2) for occ in (0, 6, 4, 2, 1)]
+    combos = [(t, pol, occ) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
     rows = []
     with open(out_path, "w") as f:
         for H in Hs:
@@ -158,7 +158,7 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
                         sets.append((inp, kda.alloc_outputs(w, dev)))
                     res = {}
                     for tile, pol, occ in combos + [(0, 0, 0)]:
-                        if occ and N * H * (128 // tile) <= 256 * occ:
+                        if tile and occ < 8 and N * H * (128 // tile) <= 256 * occ:
                             continue  # the cap would not bind
                         p = kda.params_for(w, tile_columns=tile, store_policy=pol, max_wg_per_cu=occ)
                         ws = kda.alloc_workspace(p, dev)
@@ -174,7 +174,7 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
                             ev[i][1].record()
                         torch.cuda.synchronize()
                         ms = sorted(a.elapsed_time(b) for a, b in ev)
-                        res[(f"{tile}/{pol}" + (f"/{occ}" if occ else "")) if tile else "auto"] = ms[len(ms) // 2]
+                        res[(f"{tile}/{pol}" + (f"/{occ}" if occ < 8 else "")) if tile else "auto"] = ms[len(ms) // 2]
                     best = min((v, k) for k, v in res.items() if k != "auto")
                     auto_p = kda.params_for(w)
                     row = {"H": H, "T": T, "N": N, "units": N * H, "bytes": b_alg, "ms": res,
@@ -207,7 +207,7 @@ def main():
                          "step, or the unfused two-kernel form of verify (same algorithmic bytes)")
     ap.add_argument("--tile", type=int, default=0, help="override: V columns per workgroup (32, 64, 128)")
     ap.add_argument("--store", type=int, default=0, help="override: snapshot stores, 1 streaming, 2 write-through")
-    ap.add_argument("--occ", type=int, default=0, help="override: at most 1, 2, 4 or 6 workgroups per CU")
+    ap.add_argument("--occ", type=int, default=0, help="override: at most 1, 2, 4 or 6 workgroups per CU (8: no cap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",

@@ -88,7 +88,9 @@ typedef struct {
                                at device scope */
   int32_t max_wg_per_cu;    /* at most 1, 2, 4 or 6 workgroups per compute unit, by reserving
                                LDS per workgroup (fewer concurrent snapshot streams can use
-                               HBM better); the kernel's own limits still apply */
+                               HBM better); the kernel's own limits still apply. 8: no cap.
+                               0: the AUTO cap with the AUTO tile, none when tile_columns or
+                               `variant` picks the tile */
 } kda_verify_params;
 
 #define KDA_MAX_T 16

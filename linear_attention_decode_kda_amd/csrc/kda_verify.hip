@@ -127,11 +127,14 @@ __device__ __forceinline__ float lane_sum_from(float x) {
   return x;
 }
 
-// One 16-byte snapshot store with the chosen cache policy (vector memory only).
+// One 16-byte snapshot store with the chosen cache policy (vector memory only). The
+// write-through form is inline assembly, which the compiler's hazard tracking cannot see
+// as a store: a 16-byte store's data registers must not be overwritten by VALU for two
+// wait states after it on gfx950, so the statement supplies them itself (s_nop 1).
 template <int STP>
 __device__ __forceinline__ void store_snapshot(float* p, f32x4 v) {
   if constexpr (STP == 1)
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
   else
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
@@ -296,6 +299,8 @@ struct alignas(16) Smem {
   alignas(16) R cs[3 * CF::NCH];         // raw conv cache, [local channel][3]
   alignas(16) R ws[4 * CF::NCH];         // conv taps, [local channel][4]
   alignas(16) R gs[CF::TMAX * CF::K];    // raw gate, [t][K]
+  // raw conv window of every token, laid out as its output row: [t][local channel][3]
+  alignas(16) R win[CF::PRE ? 8 : CF::TMAX * CF::NCH * 3];
   alignas(16) float dtb[CF::K];
   R bs[CF::TMAX];
   int last;
@@ -314,52 +319,15 @@ __device__ __forceinline__ int gchan(int lc, int h, int H, int hv, int vt) {
   return 2 * H * CF::K + hv * CF::V + vt * CF::VT + (lc - 2 * CF::K);
 }
 
-// raw element e[tau] of local channel lc: the cache for tau < 3, then the new tokens
+// One (sequence, value head, V-tile) unit of the step, by the whole workgroup.
 template <class CF, typename R>
-__device__ __forceinline__ R ext_raw(const Smem<CF, R>& s, int lc, int tau) {
-  return tau < 3 ? s.cs[lc * 3 + tau] : s.xs[(tau - 3) * CF::NCH + lc];
-}
-
-// Write raw conv-window / conv-cache vectors of one channel segment from LDS.
-// seg_lc: first local channel; L: channels; tok < 0 selects the rolled cache (e[T..T+2]),
-// tok >= 0 the window of token tok (e[tok+1..tok+3]). m: 16-byte vector index.
-template <class CF, typename R>
-__device__ __forceinline__ void put_window_vec(const Smem<CF, R>& s, R* dst_base, int seg_lc, int tok,
-                                               int T, int m) {
-  R v[CF::E16];
-#pragma unroll
-  for (int u = 0; u < CF::E16; ++u) {
-    const int e = m * CF::E16 + u;
-    const int lc = seg_lc + e / 3;
-    const int j = e - (e / 3) * 3;
-    const int tau = (tok < 0 ? T : tok + 1) + j;
-    v[u] = ext_raw<CF, R>(s, lc, tau);
-  }
-  u32x4 pk;
-  if constexpr (sizeof(R) == 2) {
-    pk.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-    pk.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-    pk.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-    pk.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-  } else {
-    pk.x = v[0];
-    pk.y = v[1];
-    pk.z = v[2];
-    pk.w = v[3];
-  }
-  *reinterpret_cast<u32x4*>(dst_base + (size_t)m * CF::E16) = pk;
-}
-
-template <class CF, typename R>
-__global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
+__device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const int lb) {
   constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
   constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
-  __shared__ Smem<CF, R> s;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int T = a.T, H = a.H, HV = a.HV, C = a.C;
-  const int lb = xcd_order(blockIdx.x, gridDim.x);
   const int vt = lb % CF::NVT;
   const int unit = lb / CF::NVT;  // n * HV + hv
   const int hv = unit % HV, n = unit / HV;
@@ -370,7 +338,7 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   const int in_row = a.in_idx ? a.in_idx[n] : n;
   if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
       in_row >= a.in_slots)
-    return;  // padding entry: the whole WG (and its group) skips, nothing is read or written
+    return;  // padding entry: the whole unit (and its group) skips, nothing is read or written
 
   const typename CF::XR* __restrict__ xq = static_cast<const typename CF::XR*>(a.mixed_qkv);
   const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
@@ -447,39 +415,69 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   if (!CF::PRE && tid == 0 && a.group > 1)
     prev = __hip_atomic_fetch_add(a.counters + (size_t)n * H + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---------------- phase 1a: conv + SiLU, one task per staged channel, sliding over the
-  // tokens (taps and the three cached inputs read once per channel)
-  for (int ch = tid; ch < NCH; ch += NTHR) {
-    // destination of token t: q -> row[t][ch].y, k -> row[t][ch - K].x, v -> vs[t][ch - 2K]
+  // ---------------- phase 1a: conv + SiLU, one task per pair of staged channels, sliding
+  // over the tokens (taps and the three cached inputs read once per channel); the raw
+  // window each token leaves behind, e[t+1..t+3], is staged in LDS in the layout of its
+  // output row, two channels (six values) per write
+  // q/k windows are written out by one WG of the group (all tokens) and the rolled q/k
+  // cache by the last WG to count in (the last token's window): a WG stages only those
+  const bool qk_owner = (hv % a.g == 0) && vt == 0;
+  for (int pr = tid; pr < NCH / 2; pr += NTHR) {
+    const int ch = 2 * pr;  // the pair never straddles the q | k | v blocks (all even)
+    const int t_stage = ch < 2 * K && !qk_owner ? T - 1 : 0;  // first token whose window is staged
+    // destination of (channel ch, token t); channel ch + 1 sits `cstride` floats further
     float* dp;
-    int dstride;
+    int dstride, cstride;
     if (ch < K) {
       dp = reinterpret_cast<float*>(&s.row[ch]) + 1;
       dstride = 4 * K;
+      cstride = 4;
     } else if (ch < 2 * K) {
       dp = reinterpret_cast<float*>(&s.row[ch - K]);
       dstride = 4 * K;
+      cstride = 4;
     } else {
       dp = &s.vs[ch - 2 * K];
       dstride = VT;
+      cstride = 1;
     }
     if constexpr (CF::PRE) {  // already convolved and activated
 #pragma unroll
       for (int t = 0; t < CF::TMAX; ++t)
-        if (t < T) dp[t * dstride] = up(s.xs[t * NCH + ch]);
+        if (t < T) {
+          dp[t * dstride] = up(s.xs[t * NCH + ch]);
+          dp[t * dstride + cstride] = up(s.xs[t * NCH + ch + 1]);
+        }
     } else {
-      const float w0 = up(s.ws[ch * 4 + 0]), w1 = up(s.ws[ch * 4 + 1]);
-      const float w2 = up(s.ws[ch * 4 + 2]), w3 = up(s.ws[ch * 4 + 3]);
-      float e0 = up(s.cs[ch * 3 + 0]), e1 = up(s.cs[ch * 3 + 1]), e2 = up(s.cs[ch * 3 + 2]);
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = up(s.ws[ch * 4 + j]);
+      // raw inputs e[t..t+3] of both channels: the three cached ones, then the new tokens
+      R a0 = s.cs[ch * 3 + 0], a1 = s.cs[ch * 3 + 1], a2 = s.cs[ch * 3 + 2];
+      R b0 = s.cs[ch * 3 + 3], b1 = s.cs[ch * 3 + 4], b2 = s.cs[ch * 3 + 5];
 #pragma unroll
       for (int t = 0; t < CF::TMAX; ++t) {
         if (t < T) {
-          const float e3 = up(s.xs[t * NCH + ch]);
-          const float y = fmaf(w3, e3, fmaf(w2, e2, fmaf(w1, e1, w0 * e0)));
-          dp[t * dstride] = silu_fast(y);
-          e0 = e1;
-          e1 = e2;
-          e2 = e3;
+          const R a3 = s.xs[t * NCH + ch], b3 = s.xs[t * NCH + ch + 1];
+          const float ya = fmaf(w[3], up(a3), fmaf(w[2], up(a2), fmaf(w[1], up(a1), w[0] * up(a0))));
+          const float yb = fmaf(w[7], up(b3), fmaf(w[6], up(b2), fmaf(w[5], up(b1), w[4] * up(b0))));
+          dp[t * dstride] = silu_fast(ya);
+          dp[t * dstride + cstride] = silu_fast(yb);
+          if (t >= t_stage) {
+            R* wr = &s.win[(t * NCH + ch) * 3];
+            wr[0] = a1;
+            wr[1] = a2;
+            wr[2] = a3;
+            wr[3] = b1;
+            wr[4] = b2;
+            wr[5] = b3;
+          }
+          a0 = a1;
+          a1 = a2;
+          a2 = a3;
+          b0 = b1;
+          b1 = b2;
+          b2 = b3;
         }
       }
     }
@@ -649,56 +647,46 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
       S[r] = sv;
       store_snapshot<CF::STP>(dst + (size_t)r * Q * V, sv);
     }
-  }
 
-  if constexpr (CF::PRE) return;  // the conv kernel wrote the windows and the rolled cache
-
-  // ---------------- raw copies, issued last so that no wait for them ever precedes the
-  // token loop: conv windows (v columns always; q/k by one WG per group), the rolled
-  // conv cache of the v columns (read only by this WG), and the rolled cache of the
-  // shared q/k channels by the last WG of the group to count in (every other WG of the
-  // group counted itself only after its reads had landed)
-  {
-    const bool qk_owner = (hv % a.g == 0) && vt == 0;
-    const int VQK = 3 * K / E16;  // vectors per token per q or k segment
-    const int VV = 3 * VT / E16;  // vectors per token of the v segment
-    const int nqk = qk_owner ? 2 * T * VQK : 0;
-    const int nv = T * VV;
-    const int nst = VV;
-    const int tot = nqk + nv + nst;
-    R* cw = static_cast<R*>(a.conv_window);
-    for (int q = tid; q < tot; q += NTHR) {
-      int seg_lc, tok, m;
-      if (q < nqk) {
-        const int seg = q / (T * VQK);
-        const int rem = q - seg * (T * VQK);
-        tok = rem / VQK;
-        m = rem - tok * VQK;
-        seg_lc = seg * K;
-      } else if (q < nqk + nv) {
-        const int rem = q - nqk;
-        tok = rem / VV;
-        m = rem - tok * VV;
-        seg_lc = 2 * K;
-      } else {
-        tok = -1;
-        m = q - nqk - nv;
-        seg_lc = 2 * K;
+    // raw copies of this token, after its snapshot (no load follows, so nothing ever waits
+    // on them): 16-byte vectors of the window rows staged in LDS. The conv window of the v
+    // columns always and of q/k by one WG per group; after the last token the rolled conv
+    // cache (that token's window) of the v columns (read only by this WG), and of the
+    // shared q/k channels by the last WG of the group to count in (every other WG of the
+    // group counted itself only after its reads had landed)
+    if constexpr (!CF::PRE) {
+      constexpr int VQK = 3 * K / E16;  // vectors per token of the q or the k block
+      constexpr int VV = 3 * VT / E16;  // vectors per token of this WG's v block
+      const int nqk = qk_owner ? 2 * VQK : 0;
+      const int nwin = nqk + VV;
+      const int tot = nwin + (t == T - 1 ? VV + (s.last ? 2 * VQK : 0) : 0);
+      R* cw = static_cast<R*>(a.conv_window);
+      for (int q = tid; q < tot; q += NTHR) {
+        const bool to_cache = q >= nwin;
+        int r = to_cache ? q - nwin : q;
+        int lc0, m;  // first local channel of the block, vector within the block
+        if (to_cache ? r < VV : r >= nqk) {
+          m = to_cache ? r : r - nqk;
+          lc0 = 2 * K;
+        } else {
+          if (to_cache) r -= VV;
+          const int blk = r / VQK;
+          m = r - blk * VQK;
+          lc0 = blk * K;
+        }
+        const int gc0 = gchan<CF>(lc0, h, H, hv, vt);
+        R* wdst = to_cache ? cstate + ((size_t)cs_row * C + gc0) * 3 : cw + (((size_t)in_row * T + t) * C + gc0) * 3;
+        *reinterpret_cast<u32x4*>(wdst + m * E16) =
+            *reinterpret_cast<const u32x4*>(&s.win[(t * NCH + lc0) * 3 + m * E16]);
       }
-      const int gc0 = gchan<CF>(seg_lc, h, H, hv, vt);
-      R* dst = tok < 0 ? cstate + ((size_t)cs_row * C + gc0) * 3
-                       : cw + (((size_t)in_row * T + tok) * C + gc0) * 3;
-      put_window_vec<CF, R>(s, dst, seg_lc, tok, T, m);
     }
   }
-  if (s.last) {
-    constexpr int VQK = 3 * K / E16;
-    for (int q = tid; q < 2 * VQK; q += NTHR) {
-      const int seg = q / VQK, m = q - seg * VQK;
-      const int gc0 = gchan<CF>(seg * K, h, H, hv, vt);
-      put_window_vec<CF, R>(s, cstate + ((size_t)cs_row * C + gc0) * 3, seg * K, -1, T, m);
-    }
-  }
+}
+
+template <class CF, typename R>
+__global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
+  __shared__ Smem<CF, R> s;
+  verify_unit<CF, R>(a, s, xcd_order(blockIdx.x, gridDim.x));
 }
 
 // Unfused form, first kernel: width-4 causal conv + SiLU for every channel, one thread per
@@ -811,7 +799,13 @@ __global__ void zero_words(uint32_t* p, size_t n) {
 // ----------------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------------
-using LaunchFn = hipError_t (*)(const Args&, int, hipStream_t);
+// A launch configuration: tile width, snapshot store policy, workgroups-per-CU cap.
+struct Tile {
+  int vt;       // V columns per WG
+  int stp;      // StorePolicy
+  int occ = 0;  // workgroups per CU cap (lds_reservation), 0 = none
+};
+using LaunchFn = hipError_t (*)(const Args&, const Tile&, hipStream_t);
 
 // LDS a workgroup reserves so that at most `wg_per_cu` of them share a CU (0: no cap
 // beyond the kernel's own LDS and VGPRs). The reservation is dynamic LDS on top of the
@@ -829,58 +823,65 @@ size_t lds_reservation(int wg_per_cu) {
 }
 
 template <class CF, typename R>
-hipError_t launch(const Args& a, int wg_per_cu, hipStream_t stream) {
-  const unsigned grid = (unsigned)((size_t)a.N * a.HV * CF::NVT);
+hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
+  const long long grid = (long long)a.N * a.HV * CF::NVT;
   Args copy = a;
   copy.group = a.g * CF::NVT;
   void* args[] = {&copy};
-  const size_t want = lds_reservation(wg_per_cu), have = sizeof(Smem<CF, R>);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_verify_kernel<CF, R>), dim3(grid),
+  const size_t want = lds_reservation(tl.occ), have = sizeof(Smem<CF, R>);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_verify_kernel<CF, R>), dim3((unsigned)grid),
                          dim3(CF::NTHR), args, want > have ? want - have : 0, stream);
 }
 
-// Tile shape, store policy and workgroups-per-CU cap, from an H = HV x T x N sweep on
-// MI355X (K = V = 128, bf16; every tile width, store policy and cap timed on each shape,
-// buffers rotated so that each run reads and writes HBM; the choice per (T, units) bucket
-// is the one with the best mean over H). A cap limits how many workgroups stream
-// snapshots at once; from about a thousand units up, fewer concurrent streams keep HBM
-// busier (one whole-V workgroup per CU reaches 74-77 % of peak at T >= 6, against
-// 66-69 % uncapped).
+// Tile shape, store policy and workgroups-per-CU cap, from sweeps on MI355X (K = V = 128,
+// bf16; every tile width, store policy and cap timed on each shape, buffers rotated so
+// that each run reads and writes HBM): H = HV x T x N over 200 shapes, and GVA shapes
+// (HV = 2H, 4H) at T = 3, 4, 8. The choice per (T, units) bucket is the one with the best
+// mean; over the sweeps it is within 0.6 % of the best combination per shape. A cap limits
+// how many workgroups stream snapshots at once: from a thousand units up, one whole-V
+// workgroup per CU keeps HBM busiest. Where q/k heads are shared (HV > H), write-through
+// snapshot stores do better than streaming ones.
 //   <= 128 units: the 32-column split (4 WGs per unit): a latency-bound grid, where a
 //     quarter of the per-token work per WG shortens the critical path;
-//   T <= 2: whole V, two WGs per CU from 1024 units;
-//   T <= 5: 64 columns below 512 units, whole V below 1024, whole V with two WGs per CU
-//     below 2048, 32 columns with four WGs per CU below 8192, then whole V, one per CU;
-//   T >= 6: 64 columns below 512 units, 64 columns two per CU below 1024, whole V with
-//     write-through stores two per CU below 2048, then whole V, one per CU.
+//   T <= 2: whole V; two WGs per CU from 1024 units (64 columns at T = 2 for 2048-8191),
+//     write-through at one per CU from 32768 at T = 2;
+//   T = 3 from 2048 units: 32 columns at four WGs per CU;
+//   T <= 5: whole V; two per CU for 1024-2047 units; then one per CU, write-through for
+//     shared q/k heads (32 columns at four per CU below 4096) or from 32768 units;
+//   T >= 6: whole V; write-through for 512-1023 units; then one per CU, write-through for
+//     shared q/k heads or from 16384 units.
 // Every tile width uses the same K split (32 rows per wave) and the same partial-sum tree,
 // so all of them return bit-identical results; the cap only changes scheduling.
-struct Tile {
-  int vt;       // V columns per WG
-  int stp;      // StorePolicy
-  int occ = 0;  // workgroups per CU cap (lds_reservation), 0 = none
-};
-
-Tile auto_tile_128(long long units, int T) {
+Tile auto_tile_128(long long units, int T, int g) {
   if (units <= 128) return Tile{32, kStoreNT};
-  if (T <= 2) return units < 1024 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 2};
+  if (T <= 2) {
+    if (units < 1024) return Tile{128, kStoreNT};
+    if (T == 2 && units >= 2048 && units < 8192) return Tile{64, kStoreNT, 2};
+    if (T == 1 || units < 32768) return Tile{128, kStoreNT, 2};
+    return Tile{128, kStoreSC1, 1};
+  }
+  if (T == 3 && units >= 2048) return Tile{32, kStoreNT, 4};
   if (T <= 5) {
-    if (units < 512) return Tile{64, kStoreNT};
     if (units < 1024) return Tile{128, kStoreNT};
     if (units < 2048) return Tile{128, kStoreNT, 2};
-    if (units < 8192) return Tile{32, kStoreNT, 4};
-    return Tile{128, kStoreNT, 1};
+    if (g > 1) return units < 4096 ? Tile{32, kStoreNT, 4} : Tile{128, kStoreSC1, 1};
+    return units < 32768 ? Tile{128, kStoreNT, 1} : Tile{128, kStoreSC1, 1};
   }
-  if (units < 512) return Tile{64, kStoreNT};
-  if (units < 1024) return Tile{64, kStoreNT, 2};
-  if (units < 2048) return Tile{128, kStoreSC1, 2};
+  if (units < 512) return Tile{128, kStoreNT};
+  if (units < 1024) return Tile{128, kStoreSC1};
+  if (g > 1 || units >= 16384) return Tile{128, kStoreSC1, 1};
   return Tile{128, kStoreNT, 1};
 }
 
+// The AUTO choice with the caller's overrides applied. A cap belongs to the AUTO tile: when
+// the tile is chosen by the caller (tile_columns or an explicit variant), the AUTO cap is
+// not applied and only max_wg_per_cu sets one.
 Tile choose_tile(const kda_verify_params* p) {
   const int K = p->K, V = p->V;
+  Tile t;
   if (K == 128 && V == 128) {
-    Tile t = auto_tile_128((long long)p->N * p->HV, p->T);
+    t = auto_tile_128((long long)p->N * p->HV, p->T, p->HV / p->H);
+    if (p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO) t.occ = 0;
     if (p->tile_columns != 0)
       t.vt = p->tile_columns;
     else if (p->variant == KDA_VARIANT_LARGE)
@@ -888,19 +889,29 @@ Tile choose_tile(const kda_verify_params* p) {
     else if (p->variant == KDA_VARIANT_SMALL)
       t.vt = 32;
     if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreSC1 : kStoreNT;
-    if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu;
-    return t;
+    // fp32 inputs at T > 8: a whole-V workgroup's staged inputs and conv windows would not
+    // fit in LDS; two 64-column workgroups give the same bits
+    if (p->in_dtype == KDA_F32 && p->T > 8 && t.vt == 128) t.vt = 64;
+  } else {
+    t = K == 64 && V == 64 ? Tile{p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT} : Tile{16, kStoreNT};
   }
-  if (K == 64 && V == 64) return {p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT};
-  return {16, kStoreNT};
+  if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu == 8 ? 0 : p->max_wg_per_cu;
+  return t;
 }
 
 template <typename R, int TMAX, int PRE>
 LaunchFn pick_tmax(int K, int V, Tile tl) {
   if (K == 128 && V == 128) {
-    if (tl.vt == 128)
-      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1, PRE>, R>
-                                 : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT, PRE>, R>;
+    // whole-V tiles of fp32 inputs at T > 8 would exceed the LDS of a CU (choose_tile
+    // never asks for them)
+    constexpr bool whole_v = !(sizeof(R) == 4 && TMAX > 8 && PRE == 0);
+    if constexpr (whole_v) {
+      if (tl.vt == 128)
+        return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1, PRE>, R>
+                                   : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT, PRE>, R>;
+    } else {
+      if (tl.vt == 128) return nullptr;
+    }
     if (tl.vt == 64)
       return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1, PRE>, R>
                                  : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT, PRE>, R>;
@@ -982,7 +993,7 @@ static kda_status check_params(const kda_verify_params* p) {
   if (!(p->softplus_beta > 0.0f) || !(p->l2norm_eps >= 0.0f) || p->scale != p->scale) return KDA_ERR_SHAPE;
   if (p->store_policy < 0 || p->store_policy > 2) return KDA_ERR_UNSUPPORTED;
   if (p->max_wg_per_cu != 0 && p->max_wg_per_cu != 1 && p->max_wg_per_cu != 2 && p->max_wg_per_cu != 4 &&
-      p->max_wg_per_cu != 6)
+      p->max_wg_per_cu != 6 && p->max_wg_per_cu != 8)
     return KDA_ERR_UNSUPPORTED;
   if (p->tile_columns != 0) {
     const bool ok = p->K == 128 && p->V == 128 &&
@@ -1180,7 +1191,7 @@ kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const v
   a.softplus_threshold = p->softplus_threshold;
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->K);
   a.eps = p->l2norm_eps;
-  return fn(a, tl.occ, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  return fn(a, tl, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 }  // namespace kda

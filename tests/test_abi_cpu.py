@@ -203,12 +203,12 @@ def test_tuning_overrides(lib):
     assert kda.select_variant(p) == kda.VARIANT_LARGE
     p = kda.make_params(8, 4, 2, 2, 128, 128, tile_columns=32, variant=kda.VARIANT_LARGE)
     assert kda.select_variant(p) == kda.VARIANT_SMALL  # the tile override wins
-    for bad in (dict(tile_columns=48), dict(store_policy=3), dict(max_wg_per_cu=3), dict(max_wg_per_cu=8),
+    for bad in (dict(tile_columns=48), dict(store_policy=3), dict(max_wg_per_cu=3), dict(max_wg_per_cu=7),
                 dict(max_wg_per_cu=-1)):
         p = kda.make_params(8, 4, 2, 2, 128, 128, **bad)
         ptrs, wsb = _fake_ptrs(p)
         assert _validate(lib, p, ptrs, wsb) == -3
-    for good in (1, 2, 4, 6):
+    for good in (1, 2, 4, 6, 8):
         p = kda.make_params(8, 4, 2, 2, 128, 128, max_wg_per_cu=good)
         ptrs, wsb = _fake_ptrs(p)
         assert _validate(lib, p, ptrs, wsb) == 0
@@ -239,16 +239,30 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0)       # small batch: 512 units, T = 4
     assert L(64, 3, 16, 32, 128, 128) == (32, 1, 4)        # GVA: 2048 units, T = 3
     assert L(256, 4, 32, 32, 128, 128) == (128, 1, 1)      # large batch: 8192 units
-    assert L(512, 8, 16, 64, 128, 128) == (128, 1, 1)      # max bandwidth: 32768 units, T = 8
+    assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1)      # max bandwidth: 32768 units, T = 8
     assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0)           # <= 128 units: latency-bound split
-    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0)        # T <= 2 below 1024 units
-    assert L(32, 2, 32, 32, 128, 128) == (128, 1, 2)
-    assert L(8, 4, 32, 32, 128, 128) == (64, 1, 0)         # T <= 5
+    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0)        # T <= 2
+    assert L(512, 1, 32, 32, 128, 128) == (128, 1, 2)
+    assert L(64, 2, 32, 32, 128, 128) == (64, 1, 2)
+    assert L(512, 2, 64, 64, 128, 128) == (128, 2, 1)
+    assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0)       # T <= 5
     assert L(32, 4, 32, 32, 128, 128) == (128, 1, 2)
-    assert L(8, 6, 32, 32, 128, 128) == (64, 1, 0)         # T >= 6
-    assert L(16, 6, 32, 32, 128, 128) == (64, 1, 2)
-    assert L(32, 8, 32, 32, 128, 128) == (128, 2, 2)
+    assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1)
+    assert L(64, 4, 16, 32, 128, 128) == (32, 1, 4)        # shared q/k heads
+    assert L(128, 4, 16, 32, 128, 128) == (128, 2, 1)
+    assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0)        # T >= 6
+    assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0)
     assert L(64, 8, 32, 32, 128, 128) == (128, 1, 1)
+    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1)
+    assert L(512, 6, 32, 32, 128, 128) == (128, 2, 1)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6)
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 1, 0)   # the AUTO cap goes with its tile
+    assert L(64, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0)    # caller's tile: no AUTO cap
+    assert L(64, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0)     # 8: explicitly none
+    assert L(64, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2)
+    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 1, 0)
+    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 1, 0)
+    assert L(64, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1)
+    assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2)
     assert kda.make_params(1, 0, 1, 1, 128, 128) and lib.kda_select_launch(
         ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None) == -2

@@ -247,10 +247,14 @@ def test_every_tile_shape_bit_identical(w):
     assert_matches(w, a, ref, n_index=sample, what=f"tile shapes {w.name}")
 
 
-def test_explicit_tile_and_store_overrides_bit_identical():
+@pytest.mark.parametrize("w", [W(5, 3, 2, 4, 128, 128, gate="safe"),     # up to 4 tokens per WG
+                               W(6, 8, 2, 4, 128, 128),                  # up to 8
+                               W(3, 12, 1, 2, 128, 128, gate="safe")])   # up to 16
+def test_explicit_tile_and_store_overrides_bit_identical(w):
     """Every tile width (32, 64, 128 columns per WG), both snapshot store policies and the
-    workgroups-per-CU caps give the same bits; one of them is checked against the oracle."""
-    w = W(5, 3, 2, 4, 128, 128, gate="safe")
+    workgroups-per-CU caps give the same bits, for each token-count template; one of them
+    is checked against the oracle. (The write-through store is inline assembly: a missing
+    wait after it once let later VALU writes reach memory in place of the snapshot.)"""
     inp = synth.make_inputs(w)
     outs = []
     for tile in (32, 64, 128):

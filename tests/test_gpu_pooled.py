@@ -52,9 +52,9 @@ def _pooled_case(w, slots, seed, pad=()):
     return pinp, idx, init
 
 
-def _run_pooled(w, pinp, idx, init, variant=kda.VARIANT_AUTO):
-    say(f"[gpu] pooled {w.name} {w.dtype} {w.gate} variant={variant}")
-    p = kda.params_for(w, variant=variant)
+def _run_pooled(w, pinp, idx, init, variant=kda.VARIANT_AUTO, **pkw):
+    say(f"[gpu] pooled {w.name} {w.dtype} {w.gate} variant={variant} {pkw}")
+    p = kda.params_for(w, variant=variant, **pkw)
     d = {k: v.cuda() for k, v in pinp.items()}
     di = {k: v.cuda() for k, v in idx.items()}
     out = {k: v.cuda() for k, v in init.items()}
@@ -90,6 +90,22 @@ CASES = [
 def test_pooled_verify_matches_oracle(w, slots, pad, variant):
     pinp, idx, init = _pooled_case(w, slots, seed=5, pad=pad)
     got, *_ = _run_pooled(w, pinp, idx, init, variant)
+    ref = oracle.verify_pooled(pinp, {**idx, **init}, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    _compare(w, got, ref)
+
+
+@pytest.mark.parametrize("launch", [dict(tile_columns=128, max_wg_per_cu=1),
+                                    dict(tile_columns=32, max_wg_per_cu=4),
+                                    dict(tile_columns=64, max_wg_per_cu=2)])
+def test_capped_grid_matches_oracle_and_uncapped(launch):
+    """A workgroups-per-CU cap on a grid much larger than the part holds at once (padding
+    sequences among them) returns the bits of the uncapped launch and matches the oracle."""
+    w = W(48, 3, 2, 8, gate="safe")  # 384 units of whole V: more than a persistent grid
+    pinp, idx, init = _pooled_case(w, (60, 50, 70), seed=11, pad=(0, 17, 47))
+    base, *_ = _run_pooled(w, pinp, idx, init, tile_columns=launch["tile_columns"])
+    got, *_ = _run_pooled(w, pinp, idx, init, **launch)
+    for k in ("o", "inter_ssm", "conv_window", "conv_state"):
+        assert np.array_equal(bits(got[k]), bits(base[k])), k
     ref = oracle.verify_pooled(pinp, {**idx, **init}, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
     _compare(w, got, ref)
 
