@@ -274,12 +274,18 @@ def main():
             rot[0] += 1
     elif args.op == "unfused":
         act = torch.empty((w.N, w.T, w.C), dtype=torch.float32, device=dev)
+        b_alg = synth.algorithmic_bytes(w)  # the fused step's bytes, so the fractions compare directly
+        nset = max(1, min(8, -(-(1 << 30) // b_alg)))  # rotated like the fused step
+        sets = [(inp, out)] + [({k: v.clone() for k, v in inp.items()}, kda.alloc_outputs(w, dev))
+                               for _ in range(nset - 1)]
+        rot = [0]
 
         def step():
-            kda.kda_conv_verify_decode_unfused(p, None, inp["mixed_qkv"], inp["conv_weight"], inp["conv_state"],
-                                               inp["gate"], inp["A_log"], inp["dt_bias"], inp["beta"], inp["state"],
-                                               out["o"], out["inter_ssm"], out["conv_window"], act, ws, stream)
-        b_alg = synth.algorithmic_bytes(w)  # the fused step's bytes, so the fractions compare directly
+            a, o = sets[rot[0] % nset]
+            rot[0] += 1
+            kda.kda_conv_verify_decode_unfused(p, None, a["mixed_qkv"], a["conv_weight"], a["conv_state"],
+                                               a["gate"], a["A_log"], a["dt_bias"], a["beta"], a["state"],
+                                               o["o"], o["inter_ssm"], o["conv_window"], act, ws, stream)
     else:
         # pools twice the batch, sequence rows scattered by a seeded permutation
         g = torch.Generator().manual_seed(w.seed)
