@@ -91,6 +91,10 @@ typedef struct {
                                HBM better); the kernel's own limits still apply. 8: no cap.
                                0: the AUTO cap with the AUTO tile, none when tile_columns or
                                `variant` picks the tile */
+  int32_t column_groups;    /* 1, 2 or 4: a whole-V workgroup (K = V = 128) runs as that many
+                               groups of 4 wave64s over 128/groups columns each, sharing the
+                               staged inputs and the conv (not for fp32 inputs at T > 8).
+                               0: the AUTO choice with the AUTO tile, 1 with a caller's tile */
 } kda_verify_params;
 
 #define KDA_MAX_T 16
@@ -117,11 +121,12 @@ kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream
 int32_t kda_select_variant(const kda_verify_params* p);
 
 /* The launch configuration kda_conv_verify_decode would use for these params (after the
- * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 write-through)
- * and workgroups-per-CU cap (0 = none). Host-only; any output pointer may be NULL.
- * Returns the params' validation status (outputs untouched unless KDA_OK). */
+ * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 write-through),
+ * workgroups-per-CU cap (0 = none) and column groups per workgroup. Host-only; any output
+ * pointer may be NULL. Returns the params' validation status (outputs untouched unless
+ * KDA_OK). */
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
-                             int32_t* max_wg_per_cu);
+                             int32_t* max_wg_per_cu, int32_t* column_groups);
 
 /* Validate params and pointers without launching (host-only, no HIP call). */
 kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,

@@ -210,11 +210,16 @@ constexpr int plan_half_mask(int j, int logp, int logq, int lpr) {  // lane bit 
 // PRE_ = 1: the unfused form of the step. The conv + SiLU ran in a separate kernel and
 // mixed_qkv holds its fp32 activations; this kernel only stages them (no conv cache, no
 // taps, no conv-window or conv-state writes).
-template <typename R, int K_, int V_, int VT_, int NW_, int TMAX_, int STP_ = kStoreNT, int PRE_ = 0>
+// G_ column groups: a WG covers WT = G * VT columns of V with G groups of NW waves, group g
+// taking columns [g * VT, (g + 1) * VT) exactly as a one-group WG of VT columns would (same
+// K split, same sum tree, same bits); the staging, conv, gate and l2norm are shared.
+template <typename R, int K_, int V_, int VT_, int NW_, int TMAX_, int STP_ = kStoreNT, int PRE_ = 0, int G_ = 1>
 struct Cfg {
-  static constexpr int K = K_, V = V_, VT = VT_, NW = NW_, TMAX = TMAX_, STP = STP_, PRE = PRE_;
-  static constexpr int NTHR = NW * 64;
-  static constexpr int NVT = V / VT;     // WGs per (n, hv)
+  static constexpr int K = K_, V = V_, VT = VT_, NW = NW_, TMAX = TMAX_, STP = STP_, PRE = PRE_, G = G_;
+  static constexpr int WT = G * VT;      // V columns per WG
+  static constexpr int NWT = G * NW;     // waves per WG
+  static constexpr int NTHR = NWT * 64;
+  static constexpr int NVT = V / WT;     // WGs per (n, hv)
   static constexpr int RW = K / NW;      // K rows per wave
   static constexpr int LPR = VT / 4;     // lanes across one row of the tile
   static constexpr int Q = 64 / LPR;     // rows one wave instruction covers
@@ -223,11 +228,11 @@ struct Cfg {
   static constexpr int M = P / Q;        // partials a lane holds
   static constexpr int LOGQ = Q == 1 ? 0 : Q == 2 ? 1 : Q == 4 ? 2 : Q == 8 ? 3 : 4;
   static constexpr int LOGP = P == 8 ? 3 : 4;
-  static constexpr int NCH = 2 * K + VT;        // channels a WG stages: q, k, its v columns
+  static constexpr int NCH = 2 * K + WT;        // channels a WG stages: q, k, its v columns
   static constexpr int E16 = 16 / (int)sizeof(R);  // elements per 16-byte vector
   using XR = typename std::conditional<PRE_ != 0, uint32_t, R>::type;  // staged token rows
   static constexpr int XE16 = 16 / (int)sizeof(XR);
-  static_assert(V % VT == 0 && VT % 4 == 0 && 64 % LPR == 0 && K % NW == 0, "tile shape");
+  static_assert(V % WT == 0 && VT % 4 == 0 && 64 % LPR == 0 && K % NW == 0 && NTHR <= 1024, "tile shape");
   static_assert(RW % Q == 0 && P % Q == 0 && RPL % M == 0 && (1 << LOGQ) == Q && RW % P == 0, "rows");
   static_assert(K % E16 == 0 && VT % E16 == 0 && K % 4 == 0 && K <= 128, "vector widths");
   // the partial-sum plan of this shape
@@ -291,8 +296,8 @@ __device__ __forceinline__ void reduce_partials(float (&acc)[CF::M][8]) {
 template <class CF, typename R>
 struct alignas(16) Smem {
   f32x4 row[CF::TMAX * CF::K];        // per token, per K row: {k*a, q*a, a, k} (q scaled)
-  float vs[CF::TMAX * CF::VT];        // SiLU(conv(v)) of the WG's columns
-  f32x4 part[2][CF::NW][2][CF::LPR];  // per-wave partial sums (u, w), double-buffered by token
+  float vs[CF::TMAX * CF::WT];        // SiLU(conv(v)) of the WG's columns
+  f32x4 part[2][CF::NWT][2][CF::LPR];  // per-wave partial sums (u, w), double-buffered by token
   float betas[CF::TMAX];
   float qk[CF::TMAX];
   alignas(16) typename CF::XR xs[CF::TMAX * CF::NCH];  // raw new tokens, [t][local channel]
@@ -316,7 +321,7 @@ template <class CF>
 __device__ __forceinline__ int gchan(int lc, int h, int H, int hv, int vt) {
   if (lc < CF::K) return h * CF::K + lc;
   if (lc < 2 * CF::K) return H * CF::K + h * CF::K + (lc - CF::K);
-  return 2 * H * CF::K + hv * CF::V + vt * CF::VT + (lc - 2 * CF::K);
+  return 2 * H * CF::K + hv * CF::V + vt * CF::WT + (lc - 2 * CF::K);
 }
 
 // One (sequence, value head, V-tile) unit of the step, by the whole workgroup.
@@ -393,9 +398,10 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   const R bval = bq[(size_t)(n * T + (tid < T ? tid : T - 1)) * HV + hv];
 
   // ---------------- state tile: 16-byte loads, left in flight through the prologue math
+  const int grp = wave / CF::NW, wv = wave - grp * CF::NW;  // column group, wave in the group
   const int c4 = lane % LPR, qq = lane / LPR;
-  const int col = vt * VT + c4 * 4;
-  const int row0 = wave * CF::RW + qq;  // this lane's rows: row0 + Q * r
+  const int col = vt * CF::WT + grp * VT + c4 * 4;
+  const int row0 = wv * CF::RW + qq;  // this lane's rows: row0 + Q * r
   const size_t KV = (size_t)K * V;
   const float* sp = a.state + ((size_t)st_row * HV + hv) * KV + (size_t)row0 * V + col;
   f32x4 S[RPL];
@@ -438,7 +444,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
       cstride = 4;
     } else {
       dp = &s.vs[ch - 2 * K];
-      dstride = VT;
+      dstride = CF::WT;
       cstride = 1;
     }
     if constexpr (CF::PRE) {  // already convolved and activated
@@ -510,7 +516,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   __syncthreads();  // B1
 
   // ---------------- phase 2a: q/k l2norm per token (one wave per token), fold alpha in
-  for (int t = wave; t < T; t += CF::NW) {
+  for (int t = wave; t < T; t += CF::NWT) {
     float kx[2], qx[2];
     float sk = 0.f, sq = 0.f, sqk = 0.f;
 #pragma unroll
@@ -603,17 +609,18 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
       }
     }
     __syncthreads();
-    f32x4 uu = s.part[buf][0][0][c4], ww = s.part[buf][0][1][c4];
+    const int w0 = grp * CF::NW;  // the group's first wave
+    f32x4 uu = s.part[buf][w0][0][c4], ww = s.part[buf][w0][1][c4];
     if constexpr (CF::NW == 2) {
-      uu += s.part[buf][1][0][c4];
-      ww += s.part[buf][1][1][c4];
+      uu += s.part[buf][w0 + 1][0][c4];
+      ww += s.part[buf][w0 + 1][1][c4];
     } else if constexpr (CF::NW == 4) {
-      uu = (uu + s.part[buf][1][0][c4]) + (s.part[buf][2][0][c4] + s.part[buf][3][0][c4]);
-      ww = (ww + s.part[buf][1][1][c4]) + (s.part[buf][2][1][c4] + s.part[buf][3][1][c4]);
+      uu = (uu + s.part[buf][w0 + 1][0][c4]) + (s.part[buf][w0 + 2][0][c4] + s.part[buf][w0 + 3][0][c4]);
+      ww = (ww + s.part[buf][w0 + 1][1][c4]) + (s.part[buf][w0 + 2][1][c4] + s.part[buf][w0 + 3][1][c4]);
     } else {
       static_assert(CF::NW == 1, "waves per WG");
     }
-    const f32x4 vv = *reinterpret_cast<const f32x4*>(&s.vs[t * VT + c4 * 4]);
+    const f32x4 vv = *reinterpret_cast<const f32x4*>(&s.vs[t * CF::WT + grp * VT + c4 * 4]);
     const float bt = s.betas[t], qk = s.qk[t];
     float d[4];
     d[0] = bt * (vv.x - uu.x);
@@ -622,7 +629,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
     d[3] = bt * (vv.w - uu.w);
     const size_t nth = (size_t)(n * T + t) * HV + hv;
     const size_t ith = ((size_t)in_row * T + t) * HV + hv;
-    if (wave == 0 && qq == 0)
+    if (wv == 0 && qq == 0)
       OutVec<R>::store(a.o, nth * V + col, fmaf(qk, d[0], ww.x), fmaf(qk, d[1], ww.y),
                        fmaf(qk, d[2], ww.z), fmaf(qk, d[3], ww.w));
     // S_ij <- a_i S_ij + k_i d_j, then stream the snapshot out
@@ -656,7 +663,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
     // group counted itself only after its reads had landed)
     if constexpr (!CF::PRE) {
       constexpr int VQK = 3 * K / E16;  // vectors per token of the q or the k block
-      constexpr int VV = 3 * VT / E16;  // vectors per token of this WG's v block
+      constexpr int VV = 3 * CF::WT / E16;  // vectors per token of this WG's v block
       const int nqk = qk_owner ? 2 * VQK : 0;
       const int nwin = nqk + VV;
       const int tot = nwin + (t == T - 1 ? VV + (s.last ? 2 * VQK : 0) : 0);
@@ -804,6 +811,7 @@ struct Tile {
   int vt;       // V columns per WG
   int stp;      // StorePolicy
   int occ = 0;  // workgroups per CU cap (lds_reservation), 0 = none
+  int g = 1;    // column groups of 4 waves sharing the WG's staging and conv
 };
 using LaunchFn = hipError_t (*)(const Args&, const Tile&, hipStream_t);
 
@@ -833,25 +841,28 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
                          dim3(CF::NTHR), args, want > have ? want - have : 0, stream);
 }
 
-// Tile shape, store policy and workgroups-per-CU cap, from sweeps on MI355X (K = V = 128,
-// bf16; every tile width, store policy and cap timed on each shape, buffers rotated so
-// that each run reads and writes HBM): H = HV x T x N over 200 shapes, and GVA shapes
-// (HV = 2H, 4H) at T = 3, 4, 8. The choice per (T, units) bucket is the one with the best
-// mean; over the sweeps it is within 0.6 % of the best combination per shape. A cap limits
-// how many workgroups stream snapshots at once: from a thousand units up, one whole-V
-// workgroup per CU keeps HBM busiest. Where q/k heads are shared (HV > H), write-through
-// snapshot stores do better than streaming ones.
+// Tile shape, store policy, workgroups-per-CU cap and column groups, from sweeps on MI355X
+// (K = V = 128, bf16; every combination timed on each shape, buffers rotated so that each
+// run reads and writes HBM): H = HV x T x N over 200 shapes, GVA shapes (HV = 2H, 4H), and
+// column groups on 179 shapes of 1024-32768 units. The choice per bucket is the one with
+// the best mean. A cap limits how many workgroups stream snapshots at once: from a
+// thousand units up, one whole-V workgroup per CU keeps HBM busiest. Where q/k heads are
+// shared (HV > H), write-through snapshot stores beat streaming ones at T >= 6 and at
+// 32768 units; at T = 3-5 two column groups (8 waves sharing the staging and conv) shorten
+// each workgroup's time.
 //   <= 128 units: the 32-column split (4 WGs per unit): a latency-bound grid, where a
 //     quarter of the per-token work per WG shortens the critical path;
 //   T <= 2: whole V; two WGs per CU from 1024 units (64 columns at T = 2 for 2048-8191),
 //     write-through at one per CU from 32768 at T = 2;
-//   T = 3 from 2048 units: 32 columns at four WGs per CU;
-//   T <= 5: whole V; two per CU for 1024-2047 units; then one per CU, write-through for
-//     shared q/k heads (32 columns at four per CU below 4096) or from 32768 units;
-//   T >= 6: whole V; write-through for 512-1023 units; then one per CU, write-through for
-//     shared q/k heads or from 16384 units.
-// Every tile width uses the same K split (32 rows per wave) and the same partial-sum tree,
-// so all of them return bit-identical results; the cap only changes scheduling.
+//   T <= 5: whole V below 1024 units; then one WG per CU: two column groups (T = 3,
+//     shared q/k heads below 32768, or below 4096 units), else one group, write-through
+//     from 32768;
+//   T >= 6: whole V; write-through for 512-1023 units; then one WG per CU: shared q/k
+//     heads in two column groups below 2048 units and write-through above, otherwise
+//     streaming below 16384 units and write-through from there.
+// Every tile width and grouping uses the same K split (32 rows per wave) and the same
+// partial-sum tree, so all of them return bit-identical results; the cap only changes
+// scheduling.
 Tile auto_tile_128(long long units, int T, int g) {
   if (units <= 128) return Tile{32, kStoreNT};
   if (T <= 2) {
@@ -860,17 +871,15 @@ Tile auto_tile_128(long long units, int T, int g) {
     if (T == 1 || units < 32768) return Tile{128, kStoreNT, 2};
     return Tile{128, kStoreSC1, 1};
   }
-  if (T == 3 && units >= 2048) return Tile{32, kStoreNT, 4};
   if (T <= 5) {
     if (units < 1024) return Tile{128, kStoreNT};
-    if (units < 2048) return Tile{128, kStoreNT, 2};
-    if (g > 1) return units < 4096 ? Tile{32, kStoreNT, 4} : Tile{128, kStoreSC1, 1};
+    if (T == 3 || (g > 1 && units < 32768) || units < 4096) return Tile{128, kStoreNT, 1, 2};
     return units < 32768 ? Tile{128, kStoreNT, 1} : Tile{128, kStoreSC1, 1};
   }
   if (units < 512) return Tile{128, kStoreNT};
   if (units < 1024) return Tile{128, kStoreSC1};
-  if (g > 1 || units >= 16384) return Tile{128, kStoreSC1, 1};
-  return Tile{128, kStoreNT, 1};
+  if (g > 1) return units < 2048 ? Tile{128, kStoreNT, 1, 2} : Tile{128, kStoreSC1, 1};
+  return units < 16384 ? Tile{128, kStoreNT, 1} : Tile{128, kStoreSC1, 1};
 }
 
 // The AUTO choice with the caller's overrides applied. A cap belongs to the AUTO tile: when
@@ -896,6 +905,8 @@ Tile choose_tile(const kda_verify_params* p) {
     t = K == 64 && V == 64 ? Tile{p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT} : Tile{16, kStoreNT};
   }
   if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu == 8 ? 0 : p->max_wg_per_cu;
+  if (p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO) t.g = 1;
+  if (p->column_groups != 0) t.g = p->column_groups;
   return t;
 }
 
@@ -906,12 +917,19 @@ LaunchFn pick_tmax(int K, int V, Tile tl) {
     // never asks for them)
     constexpr bool whole_v = !(sizeof(R) == 4 && TMAX > 8 && PRE == 0);
     if constexpr (whole_v) {
+      if (tl.vt == 128 && tl.g == 4)
+        return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreSC1, PRE, 4>, R>
+                                   : &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNT, PRE, 4>, R>;
+      if (tl.vt == 128 && tl.g == 2)
+        return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1, PRE, 2>, R>
+                                   : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT, PRE, 2>, R>;
       if (tl.vt == 128)
         return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1, PRE>, R>
                                    : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT, PRE>, R>;
     } else {
       if (tl.vt == 128) return nullptr;
     }
+    if (tl.g != 1) return nullptr;
     if (tl.vt == 64)
       return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1, PRE>, R>
                                  : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT, PRE>, R>;
@@ -975,6 +993,7 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
   p->tile_columns = 0;
   p->store_policy = 0;
   p->max_wg_per_cu = 0;
+  p->column_groups = 0;
 }
 
 static kda_status check_params(const kda_verify_params* p) {
@@ -995,6 +1014,14 @@ static kda_status check_params(const kda_verify_params* p) {
   if (p->max_wg_per_cu != 0 && p->max_wg_per_cu != 1 && p->max_wg_per_cu != 2 && p->max_wg_per_cu != 4 &&
       p->max_wg_per_cu != 6 && p->max_wg_per_cu != 8)
     return KDA_ERR_UNSUPPORTED;
+  if (p->column_groups != 0) {
+    // groups of 32 or 64 columns splitting a whole-V workgroup (K = V = 128)
+    const int wt = p->tile_columns != 0 ? p->tile_columns : p->variant == KDA_VARIANT_SMALL ? 32 : 128;
+    const bool ok = p->column_groups == 1 ||
+                    (p->K == 128 && p->V == 128 && wt == 128 && (p->column_groups == 2 || p->column_groups == 4) &&
+                     !(p->in_dtype == KDA_F32 && p->T > 8));
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+  }
   if (p->tile_columns != 0) {
     const bool ok = p->K == 128 && p->V == 128 &&
                     (p->tile_columns == 32 || p->tile_columns == 64 || p->tile_columns == 128);
@@ -1019,13 +1046,14 @@ int32_t kda_select_variant(const kda_verify_params* p) {
 }
 
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
-                             int32_t* max_wg_per_cu) {
+                             int32_t* max_wg_per_cu, int32_t* column_groups) {
   const kda_status st = check_params(p);
   if (st != KDA_OK) return st;
   const Tile t = choose_tile(p);
   if (tile_columns) *tile_columns = t.vt;
   if (store_policy) *store_policy = t.stp == kStoreSC1 ? 2 : 1;
   if (max_wg_per_cu) *max_wg_per_cu = t.occ;
+  if (column_groups) *column_groups = t.g;
   return KDA_OK;
 }
 

@@ -262,6 +262,9 @@ def test_explicit_tile_and_store_overrides_bit_identical(w):
             outs.append(run_gpu(w, inp, A, tile_columns=tile, store_policy=pol))
     for tile, occ in ((32, 1), (64, 2), (128, 4), (64, 6), (128, 1)):  # per-CU caps: scheduling only
         outs.append(run_gpu(w, inp, A, tile_columns=tile, max_wg_per_cu=occ))
+    for groups in (2, 4):  # whole-V workgroups split into column groups of 4 waves
+        for pol in (1, 2):
+            outs.append(run_gpu(w, inp, A, tile_columns=128, column_groups=groups, store_policy=pol, max_wg_per_cu=1))
     for o in outs[1:]:
         for k in ("o", "inter_ssm", "conv_window", "conv_state"):
             assert torch.equal(o[k], outs[0][k]), k

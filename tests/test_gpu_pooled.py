@@ -96,7 +96,8 @@ def test_pooled_verify_matches_oracle(w, slots, pad, variant):
 
 @pytest.mark.parametrize("launch", [dict(tile_columns=128, max_wg_per_cu=1),
                                     dict(tile_columns=32, max_wg_per_cu=4),
-                                    dict(tile_columns=64, max_wg_per_cu=2)])
+                                    dict(tile_columns=64, max_wg_per_cu=2),
+                                    dict(tile_columns=128, max_wg_per_cu=1, column_groups=4)])
 def test_capped_grid_matches_oracle_and_uncapped(launch):
     """A workgroups-per-CU cap on a grid much larger than the part holds at once (padding
     sequences among them) returns the bits of the uncapped launch and matches the oracle."""
