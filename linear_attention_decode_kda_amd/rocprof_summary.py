@@ -104,7 +104,8 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
              "",
              "Combinations are tile/store[/cap]: V columns per workgroup, snapshot stores (1 streaming, "
              "2 write-through), and the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed only "
-             "where the grid has more workgroups than it lets run at once). Percent of the 8 TB/s HBM "
+             "where the grid has more workgroups than it lets run at once); the AUTO choice may also "
+             "split a whole-V workgroup into column groups (gN), which the combinations do not. Percent of the 8 TB/s HBM "
              "peak = algorithmic bytes / kernel time. Shapes of <= 128 units are launch-latency-bound: "
              "their timings include the launch, and the columns differ by noise.", "",
              "| H=HV | T | N | units | best | best % | AUTO | AUTO % | AUTO/best | " + " | ".join(refs) + " |",
@@ -112,7 +113,8 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
     for r in rows:
         p = kda.make_params(r["N"], r["T"], r["H"], r["H"], 128, 128)
         ln = kda.select_launch(p)
-        auto = f"{ln['tile_columns']}/{ln['store_policy']}" + (f"/{ln['max_wg_per_cu']}" if ln["max_wg_per_cu"] else "")
+        auto = (f"{ln['tile_columns']}/{ln['store_policy']}" + (f"/{ln['max_wg_per_cu']}" if ln["max_wg_per_cu"] else "")
+                + (f" g{ln['column_groups']}" if ln["column_groups"] > 1 else ""))
         lines.append(f"| {r['H']} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | {r['best_pct']:.1f} | {auto} | "
                      f"{pct(r, 'auto'):.1f} | {r['auto_over_best']:.3f} | "
                      + " | ".join(f"{pct(r, k):.1f}" if k in r["ms"] else "-" for k in refs) + " |")
