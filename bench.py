@@ -54,6 +54,27 @@ def first_sequences(inp, n):
     return {k: (v[:n].contiguous() if k in per_seq else v) for k, v in inp.items()}
 
 
+def device_copy_gbps(nbytes: int, dev) -> float:
+    """Context for the roofline: a plain device-to-device copy moving the same number of
+    bytes (reads nbytes / 2, writes nbytes / 2), in GB/s, median of 10 timed copies."""
+    import torch
+    n = max(1, nbytes // 8)  # float32 elements read (and written)
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[5]
+    del src, dst
+    return 8 * n / (ms * 1e-3) / 1e9
+
+
 def host_threads() -> int:
     """Host threads for the all-core oracle leg: OMP_NUM_THREADS when set, else the CPU
     count, at most 16."""
@@ -352,6 +373,7 @@ def main():
 
     launch = kda.select_launch(p)
     traffic = measured_traffic(w.name, resolved, launch) if args.op == "verify" else None
+    copy_gbps = device_copy_gbps(b_alg, dev) if args.op == "verify" else None
     cpu = None
     if not args.no_cpu_baseline and args.op == "verify":
         print("[bench] timing the float64 oracle on a bounded sample (cpu_baseline)", file=sys.stderr, flush=True)
@@ -378,6 +400,7 @@ def main():
             "in_dtype": w.dtype, "state_dtype": "f32", "gate": w.gate, "variant": resolved, "launch": launch,
             "algorithmic_bytes_per_call": b_alg, "buffer_sets": nset,
             "hbm_gbps": achieved, "pct_of_hbm_peak": 100 * achieved / HBM_PEAK_GBPS,
+            "device_copy_gbps": copy_gbps,
         },
         "roofline": {
             "bound": "hbm",
