@@ -141,10 +141,12 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
 
 def sweep(out_path: str, quick: bool = False, hs=None) -> None:
     """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
-    cap (K = V = 128, bf16, softplus). Buffer sets are rotated so that at least 1 GiB is
-    touched between reuses (small shapes would otherwise run from the 256 MB last-level
-    cache). A cap is timed only where the grid has more workgroups than the cap lets run at
-    once. Writes one JSON object per shape to out_path and prints a summary line."""
+    cap on the grid schedule, and the queue schedule of whole-V workgroups at one per CU in
+    1, 2 or 4 column groups (K = V = 128, bf16, softplus). Buffer sets are rotated so that
+    at least 1 GiB is touched between reuses (small shapes would otherwise run from the
+    256 MB last-level cache). A cap is timed only where the grid has more workgroups than
+    the cap lets run at once, the queue only where there are more units than CUs. Writes
+    one JSON object per shape to out_path and prints a summary line."""
     import torch
 
     import linear_attention_decode_kda_amd as kda
@@ -154,7 +156,8 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
     Hs = tuple(hs) if hs else (8, 32) if quick else (8, 16, 32, 64)
     Ts = (2, 4, 8) if quick else (1, 2, 4, 6, 8)
     Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
-    combos = [(t, pol, occ) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
+    combos = [(t, pol, occ, 1, 1) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
+    combos += [(128, pol, 1, g, 2) for pol in (1, 2) for g in (1, 2, 4)]
     rows = []
     with open(out_path, "w") as f:
         for H in Hs:
@@ -178,10 +181,11 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
                         }
                         sets.append((inp, kda.alloc_outputs(w, dev)))
                     res = {}
-                    for tile, pol, occ in combos + [(0, 0, 0)]:
+                    for tile, pol, occ, g, sched in combos + [(0, 0, 0, 0, 0)]:
                         if tile and occ < 8 and N * H * (128 // tile) <= 256 * occ:
-                            continue  # the cap would not bind
-                        p = kda.params_for(w, tile_columns=tile, store_policy=pol, max_wg_per_cu=occ)
+                            continue  # the cap would not bind, or no unit would come from the queue
+                        p = kda.params_for(w, tile_columns=tile, store_policy=pol, max_wg_per_cu=occ,
+                                           column_groups=g, schedule=sched)
                         ws = kda.alloc_workspace(p, dev)
                         calls = [kda.PreparedVerify(p, a, o, ws) for a, o in sets]
                         for i in range(2 * nset):
@@ -195,7 +199,9 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
                             ev[i][1].record()
                         torch.cuda.synchronize()
                         ms = sorted(a.elapsed_time(b) for a, b in ev)
-                        res[(f"{tile}/{pol}" + (f"/{occ}" if occ < 8 else "")) if tile else "auto"] = ms[len(ms) // 2]
+                        key = f"{tile}/{pol}" + (f"/{occ}" if occ < 8 else "") + (f" g{g}" if g > 1 else "") + (
+                            " q" if sched == 2 else "")
+                        res[key if tile else "auto"] = ms[len(ms) // 2]
                     best = min((v, k) for k, v in res.items() if k != "auto")
                     auto_p = kda.params_for(w)
                     row = {"H": H, "T": T, "N": N, "units": N * H, "bytes": b_alg, "ms": res,
@@ -229,6 +235,9 @@ def main():
     ap.add_argument("--tile", type=int, default=0, help="override: V columns per workgroup (32, 64, 128)")
     ap.add_argument("--store", type=int, default=0, help="override: snapshot stores, 1 streaming, 2 write-through")
     ap.add_argument("--occ", type=int, default=0, help="override: at most 1, 2, 4 or 6 workgroups per CU (8: no cap)")
+    ap.add_argument("--groups", type=int, default=0, help="override: column groups of a whole-V workgroup (1, 2, 4)")
+    ap.add_argument("--schedule", type=int, default=0,
+                    help="override: 1 one workgroup per unit, 2 resident workgroups pulling units from a queue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
@@ -269,7 +278,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     variant = {"auto": kda.VARIANT_AUTO, "small": kda.VARIANT_SMALL, "large": kda.VARIANT_LARGE}[args.variant]
     p = kda.params_for(w, variant=variant, tile_columns=args.tile, store_policy=args.store,
-                       max_wg_per_cu=args.occ)
+                       max_wg_per_cu=args.occ, column_groups=args.groups, schedule=args.schedule)
     resolved = {kda.VARIANT_SMALL: "small", kda.VARIANT_LARGE: "large"}[kda.select_variant(p)]
     print(f"[bench] workload={w.name} N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V} "
           f"{w.dtype} {w.gate} variant={resolved}", file=sys.stderr, flush=True)

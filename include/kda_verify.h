@@ -95,6 +95,16 @@ typedef struct {
                                groups of 4 wave64s over 128/groups columns each, sharing the
                                staged inputs and the conv (not for fp32 inputs at T > 8).
                                0: the AUTO choice with the AUTO tile, 1 with a caller's tile */
+  int32_t schedule;         /* 1 grid: one workgroup per unit, started by the hardware as
+                               slots free up; 2 queue: only as many workgroups as are
+                               resident at once (compute units x max_wg_per_cu, or the
+                               kernel's occupancy without a cap), each pulling units from
+                               a counter in the workspace until none are left. The queue
+                               needs whole-V workgroups (with K = V = 128: tile 128, not
+                               fp32 inputs at T > 8; with K = V = 64: not the SMALL
+                               variant) and the fused step (the unfused form rejects it).
+                               0: the AUTO choice with the AUTO tile, the grid with a
+                               caller's tile */
 } kda_verify_params;
 
 #define KDA_MAX_T 16
@@ -104,10 +114,11 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
                             int32_t K, int32_t V);
 
 /* Bytes of device workspace kda_conv_verify_decode needs for these params (one
- * uint32 arrival counter per (sequence, q/k head), rounded up to 256). The counters
- * decide which workgroup writes the q/k part of conv_state, which several
- * workgroups read (PR#107 description: last-arrival counters). They must be zero
- * before the first call (kda_workspace_reset); each call leaves them zero again.
+ * uint32 arrival counter per (sequence, q/k head), then the queue schedule's two
+ * counters: units handed out and workgroups done; rounded up to 256). The arrival
+ * counters decide which workgroup writes the q/k part of conv_state, which several
+ * workgroups read (PR#107 description: last-arrival counters). All of them must be
+ * zero before the first call (kda_workspace_reset); each call leaves them zero again.
  * Returns 0 for invalid params. */
 size_t kda_workspace_bytes(const kda_verify_params* p);
 
@@ -122,11 +133,11 @@ int32_t kda_select_variant(const kda_verify_params* p);
 
 /* The launch configuration kda_conv_verify_decode would use for these params (after the
  * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 write-through),
- * workgroups-per-CU cap (0 = none) and column groups per workgroup. Host-only; any output
- * pointer may be NULL. Returns the params' validation status (outputs untouched unless
- * KDA_OK). */
+ * workgroups-per-CU cap (0 = none), column groups per workgroup and schedule (1 grid,
+ * 2 queue). Host-only; any output pointer may be NULL. Returns the params' validation
+ * status (outputs untouched unless KDA_OK). */
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
-                             int32_t* max_wg_per_cu, int32_t* column_groups);
+                             int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule);
 
 /* Validate params and pointers without launching (host-only, no HIP call). */
 kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,

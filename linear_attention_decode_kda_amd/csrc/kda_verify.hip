@@ -42,6 +42,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include <type_traits>
 
 #include "kda_verify.h"
@@ -309,6 +311,7 @@ struct alignas(16) Smem {
   alignas(16) float dtb[CF::K];
   R bs[CF::TMAX];
   int last;
+  int next[2];  // queue schedule: the unit after the current one, by iteration parity
 };
 
 template <class CF>
@@ -324,15 +327,26 @@ __device__ __forceinline__ int gchan(int lc, int h, int H, int hv, int vt) {
   return 2 * H * CF::K + hv * CF::V + vt * CF::WT + (lc - 2 * CF::K);
 }
 
-// One (sequence, value head, V-tile) unit of the step, by the whole workgroup.
-template <class CF, typename R>
-__device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const int lb) {
+// One (sequence, value head, V-tile) unit of the step, by the whole workgroup. Under the
+// queue schedule (QUEUE) thread 0 also takes a ticket for the workgroup's next unit as
+// the unit starts and leaves it in s.next[slot] before the first barrier.
+template <class CF, typename R, bool QUEUE>
+__device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const int lb, const int slot) {
   constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
   constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
 
   const int tid = threadIdx.x;
+  // The ticket is set in thread 0 only and read back from wave 0's first lane. It is left
+  // uninitialised elsewhere on purpose: any write to its register at the top of a unit
+  // (a zero, or an empty asm that defines it) makes the wave wait first for every store
+  // of the previous unit still in flight.
+  uint32_t ticket;
+  if constexpr (QUEUE)
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(a.counters + (size_t)a.N * a.H, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int wave = tid >> 6, lane = tid & 63;
   const int T = a.T, H = a.H, HV = a.HV, C = a.C;
+  __builtin_assume(T >= 1 && T <= CF::TMAX);
   const int vt = lb % CF::NVT;
   const int unit = lb / CF::NVT;  // n * HV + hv
   const int hv = unit % HV, n = unit / HV;
@@ -342,8 +356,14 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   const int st_row = a.st_idx ? a.st_idx[n] : n;
   const int in_row = a.in_idx ? a.in_idx[n] : n;
   if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
-      in_row >= a.in_slots)
-    return;  // padding entry: the whole unit (and its group) skips, nothing is read or written
+      in_row >= a.in_slots) {
+    // padding entry: the whole unit (and its group) skips, nothing is read or written
+    if constexpr (QUEUE) {
+      const int nxt = __builtin_amdgcn_readfirstlane((int)ticket);
+      if (tid == 0) s.next[slot] = nxt;
+    }
+    return;
+  }
 
   const typename CF::XR* __restrict__ xq = static_cast<const typename CF::XR*>(a.mixed_qkv);
   const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
@@ -413,6 +433,11 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   for (int k = 0; k < CF::MAXC; ++k)
     if (dsts[k] >= 0) *reinterpret_cast<u32x4*>(lds + dsts[k]) = vals[k];
   if (tid < T) s.bs[tid] = bval;
+  if constexpr (QUEUE) {
+    // the ticket was issued before the staged loads just waited for, so it has landed
+    const int nxt = __builtin_amdgcn_readfirstlane((int)ticket);
+    if (tid == 0) s.next[slot] = nxt;
+  }
   __syncthreads();  // B0: staged inputs visible; this WG's conv-cache reads have landed
 
   // q/k conv-cache ownership: count this WG in now (its reads have landed); the count
@@ -690,10 +715,40 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   }
 }
 
+// Grid schedule: one workgroup per unit; the hardware starts each workgroup as a slot on
+// a CU frees up, and hands workgroups to the XCDs round-robin, so every XCD gets the same
+// number of units whatever its speed.
 template <class CF, typename R>
 __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   __shared__ Smem<CF, R> s;
-  verify_unit<CF, R>(a, s, xcd_order(blockIdx.x, gridDim.x));
+  verify_unit<CF, R, false>(a, s, xcd_order(blockIdx.x, gridDim.x), 0);
+}
+
+// Queue schedule: only as many workgroups as are resident at once. Each takes one unit
+// of the first round by blockIdx, then keeps pulling the next unit from a counter in the
+// workspace (units handed out past the first round) until the units run out, so an XCD
+// that runs faster takes more of them, and no workgroup launch sits between units. The
+// last workgroup to leave zeroes the counter and the leave count for the next call: every
+// workgroup drew its last ticket, and saw it past the end, before it counted itself out.
+template <class CF, typename R>
+__global__ __launch_bounds__(CF::NTHR) void kda_verify_queue_kernel(const Args a) {
+  __shared__ Smem<CF, R> s;
+  const int units = a.N * a.HV * CF::NVT;
+  const int G = gridDim.x;
+  int lb = xcd_order(blockIdx.x, G);
+  for (int it = 0; lb < units; ++it) {
+    verify_unit<CF, R, true>(a, s, lb, it & 1);
+    __syncthreads();  // the unit's LDS reads are done before the next unit stages inputs
+    lb = G + s.next[it & 1];
+  }
+  if (threadIdx.x == 0) {
+    uint32_t* q = a.counters + (size_t)a.N * a.H;
+    const uint32_t left = __hip_atomic_fetch_add(q + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == (uint32_t)G - 1) {
+      __hip_atomic_store(q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // Unfused form, first kernel: width-4 causal conv + SiLU for every channel, one thread per
@@ -806,12 +861,14 @@ __global__ void zero_words(uint32_t* p, size_t n) {
 // ----------------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------------
-// A launch configuration: tile width, snapshot store policy, workgroups-per-CU cap.
+// A launch configuration: tile width, snapshot store policy, workgroups-per-CU cap,
+// column groups and schedule.
 struct Tile {
-  int vt;       // V columns per WG
-  int stp;      // StorePolicy
-  int occ = 0;  // workgroups per CU cap (lds_reservation), 0 = none
-  int g = 1;    // column groups of 4 waves sharing the WG's staging and conv
+  int vt;              // V columns per WG
+  int stp;             // StorePolicy
+  int occ = 0;         // workgroups per CU cap (lds_reservation), 0 = none
+  int g = 1;           // column groups of 4 waves sharing the WG's staging and conv
+  bool queue = false;  // resident workgroups pulling units from a counter (whole-V only)
 };
 using LaunchFn = hipError_t (*)(const Args&, const Tile&, hipStream_t);
 
@@ -830,56 +887,94 @@ size_t lds_reservation(int wg_per_cu) {
   }
 }
 
+// Workgroups of kernel `fn` that can be resident on the current device at once: the
+// compute units times the per-CU cap, or times the occupancy the runtime computes for
+// the kernel when there is no cap. 0 when the runtime cannot tell.
+long long resident_workgroups(const void* fn, int threads, size_t dyn_lds, int wg_per_cu) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cu_count[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = cu_count[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return 0;
+    cu_count[dev].store(cus, std::memory_order_relaxed);
+  }
+  int per_cu = wg_per_cu;
+  if (per_cu == 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, dyn_lds) != hipSuccess ||
+                      per_cu <= 0))
+    return 0;
+  return (long long)cus * per_cu;
+}
+
 template <class CF, typename R>
 hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
-  const long long grid = (long long)a.N * a.HV * CF::NVT;
+  const long long units = (long long)a.N * a.HV * CF::NVT;
   Args copy = a;
   copy.group = a.g * CF::NVT;
   void* args[] = {&copy};
   const size_t want = lds_reservation(tl.occ), have = sizeof(Smem<CF, R>);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_verify_kernel<CF, R>), dim3((unsigned)grid),
-                         dim3(CF::NTHR), args, want > have ? want - have : 0, stream);
+  const size_t dyn = want > have ? want - have : 0;
+  if (tl.queue) {
+    if constexpr (CF::WT == CF::V && !CF::PRE) {
+      const void* fn = reinterpret_cast<const void*>(&kda_verify_queue_kernel<CF, R>);
+      const long long slots = resident_workgroups(fn, CF::NTHR, dyn, tl.occ);
+      if (slots <= 0) return hipErrorInvalidConfiguration;
+      return hipLaunchKernel(fn, dim3((unsigned)(units < slots ? units : slots)), dim3(CF::NTHR), args, dyn, stream);
+    } else {
+      return hipErrorInvalidConfiguration;  // whole-V fused workgroups only (check_params)
+    }
+  }
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_verify_kernel<CF, R>), dim3((unsigned)units),
+                         dim3(CF::NTHR), args, dyn, stream);
 }
 
-// Tile shape, store policy, workgroups-per-CU cap and column groups, from sweeps on MI355X
-// (K = V = 128, bf16; every combination timed on each shape, buffers rotated so that each
-// run reads and writes HBM): H = HV x T x N over 200 shapes, GVA shapes (HV = 2H, 4H), and
-// column groups on 179 shapes of 1024-32768 units. The choice per bucket is the one with
-// the best mean. A cap limits how many workgroups stream snapshots at once: from a
-// thousand units up, one whole-V workgroup per CU keeps HBM busiest. Where q/k heads are
-// shared (HV > H), write-through snapshot stores beat streaming ones at T >= 6 and at
-// 32768 units; at T = 3-5 two column groups (8 waves sharing the staging and conv) shorten
-// each workgroup's time.
+// Tile shape, store policy, workgroups-per-CU cap, column groups and schedule, from sweeps
+// on MI355X (K = V = 128, bf16; every combination timed on each shape, buffers rotated so
+// that each run reads and writes HBM): H = HV x T x N over 200 shapes, GVA shapes (HV = 2H,
+// 4H), column groups on 179 shapes of 1024-32768 units, and the queue schedule against the
+// grid on 105 shapes of 2048-32768 units. The choice per bucket is the one with the best
+// mean. A cap limits how many workgroups stream snapshots at once: from a thousand units
+// up, one whole-V workgroup per CU keeps HBM busiest. From a few thousand units the queue
+// schedule (one resident workgroup per CU pulling units) beats launching a workgroup per
+// unit by 2-14 %: the XCDs no longer finish their fixed shares at different times, and no
+// workgroup launch sits between two units of a CU. Below that the queue's first round is
+// most of the work and its counter traffic does not pay.
 //   <= 128 units: the 32-column split (4 WGs per unit): a latency-bound grid, where a
 //     quarter of the per-token work per WG shortens the critical path;
-//   T <= 2: whole V; two WGs per CU from 1024 units (64 columns at T = 2 for 2048-8191),
-//     write-through at one per CU from 32768 at T = 2;
-//   T <= 5: whole V below 1024 units; then one WG per CU: two column groups (T = 3,
-//     shared q/k heads below 32768, or below 4096 units), else one group, write-through
-//     from 32768;
-//   T >= 6: whole V; write-through for 512-1023 units; then one WG per CU: shared q/k
-//     heads in two column groups below 2048 units and write-through above, otherwise
-//     streaming below 16384 units and write-through from there.
-// Every tile width and grouping uses the same K split (32 rows per wave) and the same
-// partial-sum tree, so all of them return bit-identical results; the cap only changes
-// scheduling.
+//   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
+//     groups; T >= 2 from 4096 units (T = 3 without shared heads from 8192): two column
+//     groups at T = 2 (and T = 3 below 8192), else one; write-through stores at T = 3-4
+//     from 32768 units, T = 6-7 from 16384, T >= 8 from 16384 or with shared q/k heads;
+//   otherwise the grid, whole V:
+//   T <= 2: two WGs per CU from 1024 units (64 columns at T = 2 from 2048);
+//   T <= 5: from 1024 units one WG per CU in two column groups;
+//   T >= 6: write-through for 512-1023 units; then one WG per CU: shared q/k heads in two
+//     column groups below 2048 units and write-through above, otherwise streaming.
+// Every tile width, grouping and schedule uses the same K split (32 rows per wave) and the
+// same partial-sum tree, so all of them return bit-identical results; the cap and the
+// schedule only change which CU runs a unit, and when.
 Tile auto_tile_128(long long units, int T, int g) {
   if (units <= 128) return Tile{32, kStoreNT};
+  // queue schedule, one whole-V workgroup per CU
+  if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
+  if (T >= 2 && units >= 4096 && !(T == 3 && g == 1 && units < 8192)) {
+    if (T == 2 || (T == 3 && units < 8192)) return Tile{128, kStoreNT, 1, 2, true};
+    if (T <= 5) return Tile{128, T <= 4 && units >= 32768 ? kStoreSC1 : kStoreNT, 1, 1, true};
+    if (T <= 7) return Tile{128, units >= 16384 ? kStoreSC1 : kStoreNT, 1, 1, true};
+    return Tile{128, g == 1 && units < 16384 ? kStoreNT : kStoreSC1, 1, 1, true};
+  }
+  // the grid
   if (T <= 2) {
     if (units < 1024) return Tile{128, kStoreNT};
-    if (T == 2 && units >= 2048 && units < 8192) return Tile{64, kStoreNT, 2};
-    if (T == 1 || units < 32768) return Tile{128, kStoreNT, 2};
-    return Tile{128, kStoreSC1, 1};
+    return T == 2 && units >= 2048 ? Tile{64, kStoreNT, 2} : Tile{128, kStoreNT, 2};
   }
-  if (T <= 5) {
-    if (units < 1024) return Tile{128, kStoreNT};
-    if (T == 3 || (g > 1 && units < 32768) || units < 4096) return Tile{128, kStoreNT, 1, 2};
-    return units < 32768 ? Tile{128, kStoreNT, 1} : Tile{128, kStoreSC1, 1};
-  }
+  if (T <= 5) return units < 1024 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 1, 2};
   if (units < 512) return Tile{128, kStoreNT};
   if (units < 1024) return Tile{128, kStoreSC1};
   if (g > 1) return units < 2048 ? Tile{128, kStoreNT, 1, 2} : Tile{128, kStoreSC1, 1};
-  return units < 16384 ? Tile{128, kStoreNT, 1} : Tile{128, kStoreSC1, 1};
+  return Tile{128, kStoreNT, 1};
 }
 
 // The AUTO choice with the caller's overrides applied. A cap belongs to the AUTO tile: when
@@ -887,26 +982,37 @@ Tile auto_tile_128(long long units, int T, int g) {
 // not applied and only max_wg_per_cu sets one.
 Tile choose_tile(const kda_verify_params* p) {
   const int K = p->K, V = p->V;
+  const bool caller_tile = p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO;
   Tile t;
   if (K == 128 && V == 128) {
     t = auto_tile_128((long long)p->N * p->HV, p->T, p->HV / p->H);
-    if (p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO) t.occ = 0;
+    if (caller_tile) {
+      t.occ = 0;
+      t.g = 1;
+      t.queue = false;
+    }
     if (p->tile_columns != 0)
       t.vt = p->tile_columns;
     else if (p->variant == KDA_VARIANT_LARGE)
       t.vt = 128;
     else if (p->variant == KDA_VARIANT_SMALL)
       t.vt = 32;
+    else if (p->schedule == 2)
+      t.vt = 128;  // the queue runs whole-V workgroups
     if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreSC1 : kStoreNT;
     // fp32 inputs at T > 8: a whole-V workgroup's staged inputs and conv windows would not
     // fit in LDS; two 64-column workgroups give the same bits
-    if (p->in_dtype == KDA_F32 && p->T > 8 && t.vt == 128) t.vt = 64;
+    if (p->in_dtype == KDA_F32 && p->T > 8 && t.vt == 128) {
+      t.vt = 64;
+      t.g = 1;
+      t.queue = false;
+    }
   } else {
     t = K == 64 && V == 64 ? Tile{p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT} : Tile{16, kStoreNT};
   }
   if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu == 8 ? 0 : p->max_wg_per_cu;
-  if (p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO) t.g = 1;
   if (p->column_groups != 0) t.g = p->column_groups;
+  if (p->schedule != 0) t.queue = p->schedule == 2;
   return t;
 }
 
@@ -994,6 +1100,7 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
   p->store_policy = 0;
   p->max_wg_per_cu = 0;
   p->column_groups = 0;
+  p->schedule = 0;
 }
 
 static kda_status check_params(const kda_verify_params* p) {
@@ -1027,13 +1134,25 @@ static kda_status check_params(const kda_verify_params* p) {
                     (p->tile_columns == 32 || p->tile_columns == 64 || p->tile_columns == 128);
     if (!ok) return KDA_ERR_UNSUPPORTED;
   }
+  if (p->schedule < 0 || p->schedule > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->schedule == 2) {
+    // the queue runs whole-V workgroups
+    bool ok = true;
+    if (p->K == 128) {
+      const int wt = p->tile_columns != 0 ? p->tile_columns : p->variant == KDA_VARIANT_SMALL ? 32 : 128;
+      ok = wt == 128 && !(p->in_dtype == KDA_F32 && p->T > 8);
+    } else if (p->K == 64) {
+      ok = p->variant != KDA_VARIANT_SMALL;
+    }
+    if (!ok) return KDA_ERR_UNSUPPORTED;
+  }
   return KDA_OK;
 }
 
 size_t kda_workspace_bytes(const kda_verify_params* p) {
   if (check_params(p) != KDA_OK) return 0;
-  size_t words = (size_t)p->N * p->H;
-  if (words == 0) words = 1;
+  // an arrival counter per (sequence, q/k head), then the queue's ticket and leave counts
+  const size_t words = (size_t)p->N * p->H + 2;
   return (words * 4 + 255) / 256 * 256;
 }
 
@@ -1046,7 +1165,7 @@ int32_t kda_select_variant(const kda_verify_params* p) {
 }
 
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
-                             int32_t* max_wg_per_cu, int32_t* column_groups) {
+                             int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule) {
   const kda_status st = check_params(p);
   if (st != KDA_OK) return st;
   const Tile t = choose_tile(p);
@@ -1054,6 +1173,7 @@ kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, 
   if (store_policy) *store_policy = t.stp == kStoreSC1 ? 2 : 1;
   if (max_wg_per_cu) *max_wg_per_cu = t.occ;
   if (column_groups) *column_groups = t.g;
+  if (schedule) *schedule = t.queue ? 2 : 1;
   return KDA_OK;
 }
 
@@ -1184,7 +1304,8 @@ kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const v
                          const void* conv_weight, void* conv_state, const void* gate, const float* A_log,
                          const float* dt_bias, const void* beta, const float* state, void* o, float* inter_ssm,
                          void* conv_window, void* workspace, hipStream_t stream, bool pre) {
-  const Tile tl = choose_tile(p);
+  Tile tl = choose_tile(p);
+  if (pre) tl.queue = false;  // the unfused form keeps one workgroup per unit
   LaunchFn fn = pick_launch(p, tl, pre);
   if (!fn) return KDA_ERR_UNSUPPORTED;
   Args a;
@@ -1236,6 +1357,7 @@ kda_status kda_conv_verify_decode_unfused(const kda_verify_params* p, const kda_
   kda_status st = validate_verify(p, pools, &pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta,
                                   state, o, inter_ssm, conv_window, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
+  if (p->schedule == 2) return KDA_ERR_UNSUPPORTED;
   if (p->N == 0) return KDA_OK;
   if (!act) return KDA_ERR_NULL;
   if (misaligned(act)) return KDA_ERR_ALIGN;

@@ -19,7 +19,7 @@ import statistics
 import sys
 
 COPY_BYTES = 1 << 30
-KERNEL_TAG = "kda_verify_kernel"
+KERNEL_TAG = "kda::kda_verify"  # the grid kernel (kda_verify_kernel) and the queue kernel
 
 
 def _rows(path):
@@ -96,16 +96,17 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
 
     rows = [json.loads(ln) for ln in open(jsonl) if ln.strip()]
     pct = lambda r, k: 100.0 * r["bytes"] / r["ms"][k] / 1e6 / 8000.0 if k in r["ms"] else float("nan")
-    refs = ("32/1", "128/1", "128/1/1")
+    refs = ("32/1", "128/1", "128/1/1", "128/1/1 q")
     lines = ["# H = HV x T x N sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
              f"Command: `{cmd}` (one MI355X; each shape's buffers rotated so that >= 1 GiB is touched "
              "between reuses; median of >= 8 calls per combination), summarised by "
              f"`python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md {os.path.basename(jsonl)} ...`.",
              "",
-             "Combinations are tile/store[/cap]: V columns per workgroup, snapshot stores (1 streaming, "
-             "2 write-through), and the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed only "
-             "where the grid has more workgroups than it lets run at once); the AUTO choice may also "
-             "split a whole-V workgroup into column groups (gN), which the combinations do not. Percent of the 8 TB/s HBM "
+             "Combinations are tile/store[/cap][ gN][ q]: V columns per workgroup, snapshot stores (1 "
+             "streaming, 2 write-through), the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed "
+             "only where the grid has more workgroups than it lets run at once), column groups of a "
+             "whole-V workgroup (gN), and q for the queue schedule (resident workgroups pulling units; "
+             "otherwise one workgroup per unit). Percent of the 8 TB/s HBM "
              "peak = algorithmic bytes / kernel time. Shapes of <= 128 units are launch-latency-bound: "
              "their timings include the launch, and the columns differ by noise.", "",
              "| H=HV | T | N | units | best | best % | AUTO | AUTO % | AUTO/best | " + " | ".join(refs) + " |",
@@ -114,7 +115,8 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
         p = kda.make_params(r["N"], r["T"], r["H"], r["H"], 128, 128)
         ln = kda.select_launch(p)
         auto = (f"{ln['tile_columns']}/{ln['store_policy']}" + (f"/{ln['max_wg_per_cu']}" if ln["max_wg_per_cu"] else "")
-                + (f" g{ln['column_groups']}" if ln["column_groups"] > 1 else ""))
+                + (f" g{ln['column_groups']}" if ln["column_groups"] > 1 else "")
+                + (" q" if ln.get("schedule") == 2 else ""))
         lines.append(f"| {r['H']} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | {r['best_pct']:.1f} | {auto} | "
                      f"{pct(r, 'auto'):.1f} | {r['auto_over_best']:.3f} | "
                      + " | ".join(f"{pct(r, k):.1f}" if k in r["ms"] else "-" for k in refs) + " |")

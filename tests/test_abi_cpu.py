@@ -47,8 +47,10 @@ def test_params_init_defaults(lib):
 
 
 def test_workspace_bytes(lib):
-    assert kda.workspace_bytes(kda.make_params(256, 4, 32, 32, 128, 128)) == 256 * 32 * 4
+    # one arrival counter per (sequence, q/k head) and the queue's two counters, in 256 B
+    assert kda.workspace_bytes(kda.make_params(256, 4, 32, 32, 128, 128)) == 256 * 32 * 4 + 256
     assert kda.workspace_bytes(kda.make_params(3, 1, 2, 4, 128, 128)) == 256
+    assert kda.workspace_bytes(kda.make_params(0, 1, 2, 4, 128, 128)) == 256
     assert kda.workspace_bytes(kda.make_params(3, 1, 2, 3, 128, 128)) == 0  # invalid: HV % H
 
 
@@ -206,7 +208,9 @@ def test_tuning_overrides(lib):
     for bad in (dict(tile_columns=48), dict(store_policy=3), dict(max_wg_per_cu=3), dict(max_wg_per_cu=7),
                 dict(max_wg_per_cu=-1), dict(column_groups=3), dict(column_groups=8),
                 dict(tile_columns=64, column_groups=2), dict(variant=kda.VARIANT_SMALL, column_groups=4),
-                dict(dtype="f32", T=12, column_groups=2)):
+                dict(dtype="f32", T=12, column_groups=2), dict(schedule=3), dict(schedule=-1),
+                dict(tile_columns=64, schedule=2), dict(variant=kda.VARIANT_SMALL, schedule=2),
+                dict(dtype="f32", T=12, schedule=2)):
         kw = dict(bad)
         p = kda.make_params(8, kw.pop("T", 4), 2, 2, 128, 128, **kw)
         ptrs, wsb = _fake_ptrs(p)
@@ -218,6 +222,13 @@ def test_tuning_overrides(lib):
     p = kda.make_params(8, 4, 2, 2, 64, 64, tile_columns=64)  # overrides exist for K = V = 128 only
     ptrs, wsb = _fake_ptrs(p)
     assert _validate(lib, p, ptrs, wsb) == -3
+    p = kda.make_params(8, 4, 2, 2, 64, 64, variant=kda.VARIANT_SMALL, schedule=2)  # the queue takes whole V
+    ptrs, wsb = _fake_ptrs(p)
+    assert _validate(lib, p, ptrs, wsb) == -3
+    for good in (dict(schedule=1), dict(schedule=2), dict(schedule=2, max_wg_per_cu=2, column_groups=4)):
+        p = kda.make_params(8, 4, 2, 2, 128, 128, **good)
+        ptrs, wsb = _fake_ptrs(p)
+        assert _validate(lib, p, ptrs, wsb) == 0, good
 
 
 def test_prepared_call_checks_arguments_once():
@@ -235,44 +246,65 @@ def test_prepared_call_checks_arguments_once():
 
 
 def test_select_launch_follows_the_dispatch_rule(lib):
-    """The AUTO rule (tile, stores, workgroups-per-CU cap) on the named workloads and at
-    the edges of its buckets, and the overrides winning over it."""
+    """The AUTO rule (tile, stores, workgroups-per-CU cap, column groups, schedule: 1 grid,
+    2 queue) on the named workloads and at the edges of its buckets, and the overrides
+    winning over it."""
     L = lambda *shape, **kw: tuple(kda.select_launch(kda.make_params(*shape, **kw)).values())
-    assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0, 1)            # tiny: the only K = V = 16 tile
-    assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0, 1)       # small batch: 512 units, T = 4
-    assert L(64, 3, 16, 32, 128, 128) == (128, 1, 1, 2)       # GVA: 2048 units, T = 3
-    assert L(256, 4, 32, 32, 128, 128) == (128, 1, 1, 1)      # large batch: 8192 units
-    assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1)      # max bandwidth: 32768 units, T = 8
-    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1)           # <= 128 units: latency-bound split
-    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 1)        # T <= 2
-    assert L(512, 1, 32, 32, 128, 128) == (128, 1, 2, 1)
-    assert L(64, 2, 32, 32, 128, 128) == (64, 1, 2, 1)
-    assert L(512, 2, 64, 64, 128, 128) == (128, 2, 1, 1)
-    assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0, 1)       # T <= 5
-    assert L(32, 4, 32, 32, 128, 128) == (128, 1, 1, 2)
-    assert L(128, 4, 32, 32, 128, 128) == (128, 1, 1, 1)
-    assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1)
-    assert L(512, 3, 32, 32, 128, 128) == (128, 1, 1, 2)
-    assert L(128, 4, 16, 32, 128, 128) == (128, 1, 1, 2)      # shared q/k heads
-    assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1)
-    assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0, 1)        # T >= 6
-    assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1)
-    assert L(64, 8, 32, 32, 128, 128) == (128, 1, 1, 1)
-    assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2)
-    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1)
-    assert L(512, 6, 32, 32, 128, 128) == (128, 2, 1, 1)
-    assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6, 1)
-    assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 1, 0, 1)   # the AUTO cap goes with its tile
-    assert L(64, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1)  # caller's tile: no AUTO cap
-    assert L(64, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0, 2)   # 8: explicitly none
-    assert L(64, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2, 1)
-    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 1, 0, 1)
-    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 1, 0, 1)
-    assert L(64, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1, 2)
-    assert L(64, 4, 32, 32, 128, 128, column_groups=4) == (128, 1, 1, 4)
-    assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2, 1)
+    assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0, 1, 1)            # tiny: the only K = V = 16 tile
+    assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0, 1, 1)       # small batch: 512 units, T = 4
+    assert L(64, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # GVA: 2048 units, T = 3
+    assert L(256, 4, 32, 32, 128, 128) == (128, 1, 1, 1, 2)      # large batch: 8192 units
+    assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 2)      # max bandwidth: 32768 units, T = 8
+    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)           # <= 128 units: latency-bound split
+    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)        # T <= 2
+    assert L(32, 1, 32, 32, 128, 128) == (128, 1, 2, 1, 1)
+    assert L(64, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)       # T = 1 queue from 2048 units
+    assert L(64, 1, 16, 32, 128, 128) == (128, 1, 2, 1, 1)       # ... not with shared q/k heads
+    assert L(512, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)
+    assert L(64, 2, 32, 32, 128, 128) == (64, 1, 2, 1, 1)
+    assert L(128, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2 queue from 4096 units
+    assert L(512, 2, 64, 64, 128, 128) == (128, 1, 1, 2, 2)
+    assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T <= 5
+    assert L(32, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(128, 4, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(128, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T = 3: the grid below 8192 ...
+    assert L(256, 3, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(128, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 2)      # ... unless q/k heads are shared
+    assert L(512, 3, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(128, 4, 16, 32, 128, 128) == (128, 1, 1, 1, 2)      # shared q/k heads
+    assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0, 1, 1)        # T >= 6
+    assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(64, 8, 32, 32, 128, 128) == (128, 1, 1, 1, 1)
+    assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
+    assert L(128, 8, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(256, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(256, 6, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(512, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6, 1, 1)
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 1, 0, 1, 1)   # the AUTO cap goes with its tile
+    assert L(64, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: no AUTO cap
+    assert L(64, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0, 2, 1)   # 8: explicitly none
+    assert L(64, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2, 1, 1)
+    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 1, 0, 1, 1)
+    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 1, 0, 1, 1)
+    assert L(64, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1, 2, 1)
+    assert L(64, 4, 32, 32, 128, 128, column_groups=4) == (128, 1, 1, 4, 1)
+    assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2, 1, 1)
+    assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 1, 1, 1, 1)      # the grid, AUTO cap kept
+    assert L(64, 4, 32, 32, 128, 128, schedule=2) == (128, 1, 1, 2, 2)
+    assert L(1, 4, 8, 8, 128, 128, schedule=2) == (128, 1, 0, 1, 2)          # the queue takes whole V
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 1, 0, 1, 2)
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: the grid
+    assert L(3, 16, 1, 4, 64, 64, schedule=2) == (64, 1, 0, 1, 2)
+    # fp32 at T > 8: two 64-column workgroups, one group each, on the grid
+    assert L(64, 9, 8, 16, 128, 128, dtype="f32") == (64, 1, 1, 1, 1)
+    assert L(512, 9, 32, 32, 128, 128, dtype="f32") == (64, 2, 1, 1, 1)
     assert kda.make_params(1, 0, 1, 1, 128, 128) and lib.kda_select_launch(
-        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None, None) == -2
+        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None, None, None) == -2
     G = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["column_groups"]
     assert G(256, 4, 32, 32, 128, 128, column_groups=4) == 4
     assert G(256, 4, 32, 32, 128, 128, tile_columns=128) == 1     # caller's tile: one group unless asked

@@ -251,8 +251,9 @@ def test_every_tile_shape_bit_identical(w):
                                W(6, 8, 2, 4, 128, 128),                  # up to 8
                                W(3, 12, 1, 2, 128, 128, gate="safe")])   # up to 16
 def test_explicit_tile_and_store_overrides_bit_identical(w):
-    """Every tile width (32, 64, 128 columns per WG), both snapshot store policies and the
-    workgroups-per-CU caps give the same bits, for each token-count template; one of them
+    """Every tile width (32, 64, 128 columns per WG), both snapshot store policies, the
+    workgroups-per-CU caps and both schedules give the same bits, for each token-count
+    template; one of them
     is checked against the oracle. (The write-through store is inline assembly: a missing
     wait after it once let later VALU writes reach memory in place of the snapshot.)"""
     inp = synth.make_inputs(w)
@@ -265,6 +266,9 @@ def test_explicit_tile_and_store_overrides_bit_identical(w):
     for groups in (2, 4):  # whole-V workgroups split into column groups of 4 waves
         for pol in (1, 2):
             outs.append(run_gpu(w, inp, A, tile_columns=128, column_groups=groups, store_policy=pol, max_wg_per_cu=1))
+    for groups, pol, occ in ((1, 1, 1), (2, 2, 1), (4, 1, 8)):  # the queue schedule
+        outs.append(run_gpu(w, inp, A, tile_columns=128, column_groups=groups, store_policy=pol, max_wg_per_cu=occ,
+                            schedule=2))
     for o in outs[1:]:
         for k in ("o", "inter_ssm", "conv_window", "conv_state"):
             assert torch.equal(o[k], outs[0][k]), k

@@ -97,10 +97,13 @@ def test_pooled_verify_matches_oracle(w, slots, pad, variant):
 @pytest.mark.parametrize("launch", [dict(tile_columns=128, max_wg_per_cu=1),
                                     dict(tile_columns=32, max_wg_per_cu=4),
                                     dict(tile_columns=64, max_wg_per_cu=2),
-                                    dict(tile_columns=128, max_wg_per_cu=1, column_groups=4)])
+                                    dict(tile_columns=128, max_wg_per_cu=1, column_groups=4),
+                                    dict(tile_columns=128, max_wg_per_cu=1, schedule=2),
+                                    dict(tile_columns=128, max_wg_per_cu=1, column_groups=2, schedule=2)])
 def test_capped_grid_matches_oracle_and_uncapped(launch):
     """A workgroups-per-CU cap on a grid much larger than the part holds at once (padding
-    sequences among them) returns the bits of the uncapped launch and matches the oracle."""
+    sequences among them), or the queue schedule pulling those units (padding units skip
+    and hand on their ticket), returns the bits of the uncapped grid and matches the oracle."""
     w = W(48, 3, 2, 8, gate="safe")  # 384 units of whole V: more than a persistent grid
     pinp, idx, init = _pooled_case(w, (60, 50, 70), seed=11, pad=(0, 17, 47))
     base, *_ = _run_pooled(w, pinp, idx, init, tile_columns=launch["tile_columns"])
