@@ -19,19 +19,21 @@ from gpu_util import assert_matches, run_gpu, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _setup(w, variant=kda.VARIANT_AUTO):
+def _setup(w, variant=kda.VARIANT_AUTO, **pkw):
     inp = synth.make_inputs(w)
     g = to_dev(inp)
-    p = kda.params_for(w, variant=variant)
+    p = kda.params_for(w, variant=variant, **pkw)
     ws = kda.alloc_workspace(p)
     out = kda.alloc_outputs(w)
     return inp, g, p, ws, out
 
 
-@pytest.mark.parametrize("name,reps", [("small_batch", 10000), ("gva", 2000)])
+@pytest.mark.parametrize("name,reps", [("small_batch", 10000), ("gva", 2000), ("large_batch", 10000)])
 def test_determinism_repeats(name, reps):
     """Repeated calls on the same inputs give bitwise identical outputs. conv_state is
-    rolled in place, so it is restored from a pristine copy before each call."""
+    rolled in place, so it is restored from a pristine copy before each call. On
+    large_batch AUTO runs the queue schedule, whose unit-to-CU assignment changes from
+    call to call while the bits must not (and whose counters must reset every call)."""
     w = synth.WORKLOADS[name]
     say(f"[gpu] determinism {name} x{reps}")
     inp, g, p, ws, out = _setup(w)
@@ -164,10 +166,14 @@ def test_stale_counters_recovered_by_reset():
     assert_matches(w, {**out, "conv_state": g["conv_state"]}, oracle.verify_workload(w, inp), what="after reset")
 
 
-def test_non_default_stream_and_concurrent_calls():
-    wa = synth.WORKLOADS["gva"].with_(N=6)
+@pytest.mark.parametrize("qa", [0, 2])
+def test_non_default_stream_and_concurrent_calls(qa):
+    """Overlapping calls on two streams with their own workspaces; with qa = 2 the first
+    runs the queue schedule over 2048 units while the second runs beside it."""
+    wa = synth.WORKLOADS["gva"].with_(N=64 if qa else 6)
     wb = synth.WORKLOADS["small_batch"].with_(N=5, seed=77)
-    ia, ga, pa, wsa, oa = _setup(wa)
+    say(f"[gpu] two streams, schedule {qa}")
+    ia, ga, pa, wsa, oa = _setup(wa, schedule=qa)
     ib, gb, pb, wsb, ob = _setup(wb)
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -188,11 +194,15 @@ def test_non_default_stream_and_concurrent_calls():
     assert_matches(wb, {**ob, "conv_state": gb["conv_state"]}, oracle.verify_workload(wb, ib), what="stream b")
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("N,sched", [(8, 0), (64, 2)])
+def test_graph_replay_matches_eager(N, sched):
     """Capture one call in a HIP graph; every replay (conv_state restored eagerly in
-    between) equals the eager result bit for bit."""
-    w = synth.WORKLOADS["gva"].with_(N=8)
-    inp, g, p, ws, out = _setup(w)
+    between) equals the eager result bit for bit. With the queue schedule (2048 units over
+    the resident workgroups) each replay also relies on the previous one having zeroed the
+    queue counters."""
+    w = synth.WORKLOADS["gva"].with_(N=N)
+    say(f"[gpu] graph replay gva N={N} schedule {sched}")
+    inp, g, p, ws, out = _setup(w, schedule=sched)
     cs0 = g["conv_state"].clone()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
