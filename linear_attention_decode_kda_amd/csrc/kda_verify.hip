@@ -941,22 +941,24 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 // unit by 2-14 %: the XCDs no longer finish their fixed shares at different times, and no
 // workgroup launch sits between two units of a CU. Below that the queue's first round is
 // most of the work and its counter traffic does not pay.
-//   <= 128 units: the 32-column split (4 WGs per unit): a latency-bound grid, where a
-//     quarter of the per-token work per WG shortens the critical path;
 //   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
 //     groups; T >= 2 from 4096 units (T = 3 without shared heads from 8192): two column
 //     groups at T = 2 (and T = 3 below 8192), else one; write-through stores at T = 3-4
 //     from 32768 units, T = 6-7 from 16384, T >= 8 from 16384 or with shared q/k heads;
-//   otherwise the grid, whole V:
-//   T <= 2: two WGs per CU from 1024 units (64 columns at T = 2 from 2048);
-//   T <= 5: from 1024 units one WG per CU in two column groups;
-//   T >= 6: write-through for 512-1023 units; then one WG per CU: shared q/k heads in two
-//     column groups below 2048 units and write-through above, otherwise streaming.
+//   otherwise the grid. Below 1024 units (a sweep of 100 shapes of 128-768 units, T = 1-8,
+//     three timings each), where one generation of workgroups is most of the call and
+//     shorter per-unit chains pay:
+//     <= 64 units, and <= 128 at T = 2: the 32-column split (4 WGs per unit);
+//     <= 128 units: whole V in four column groups; 129-447: whole V in two column groups
+//     (T = 1: four below 320 units, else one); 448-512: whole V, write-through at T >= 6;
+//     513-1023: whole V at T = 1, write-through at T = 2, else one WG per CU in two groups;
+//   from 1024 units, whole V: T <= 2: two WGs per CU (64 columns at T = 2 from 2048);
+//     T <= 5: one WG per CU in two column groups; T >= 6: one WG per CU: shared q/k heads
+//     in two column groups below 2048 units and write-through above, otherwise streaming.
 // Every tile width, grouping and schedule uses the same K split (32 rows per wave) and the
 // same partial-sum tree, so all of them return bit-identical results; the cap and the
 // schedule only change which CU runs a unit, and when.
 Tile auto_tile_128(long long units, int T, int g) {
-  if (units <= 128) return Tile{32, kStoreNT};
   // queue schedule, one whole-V workgroup per CU
   if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
   if (T >= 2 && units >= 4096 && !(T == 3 && g == 1 && units < 8192)) {
@@ -965,14 +967,15 @@ Tile auto_tile_128(long long units, int T, int g) {
     if (T <= 7) return Tile{128, units >= 16384 ? kStoreSC1 : kStoreNT, 1, 1, true};
     return Tile{128, g == 1 && units < 16384 ? kStoreNT : kStoreSC1, 1, 1, true};
   }
-  // the grid
-  if (T <= 2) {
-    if (units < 1024) return Tile{128, kStoreNT};
-    return T == 2 && units >= 2048 ? Tile{64, kStoreNT, 2} : Tile{128, kStoreNT, 2};
-  }
-  if (T <= 5) return units < 1024 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 1, 2};
-  if (units < 512) return Tile{128, kStoreNT};
-  if (units < 1024) return Tile{128, kStoreSC1};
+  // the grid: below 1024 units
+  if (units <= 64 || (units <= 128 && T == 2)) return Tile{32, kStoreNT};
+  if (units <= 128) return Tile{128, kStoreNT, 0, 4};
+  if (units < 448) return Tile{128, kStoreNT, 0, T > 1 ? 2 : units < 320 ? 4 : 1};
+  if (units <= 512) return Tile{128, T >= 6 ? kStoreSC1 : kStoreNT};
+  if (units < 1024) return T == 1 ? Tile{128, kStoreNT} : T == 2 ? Tile{128, kStoreSC1} : Tile{128, kStoreNT, 1, 2};
+  // the grid from 1024 units
+  if (T <= 2) return T == 2 && units >= 2048 ? Tile{64, kStoreNT, 2} : Tile{128, kStoreNT, 2};
+  if (T <= 5) return Tile{128, kStoreNT, 1, 2};
   if (g > 1) return units < 2048 ? Tile{128, kStoreNT, 1, 2} : Tile{128, kStoreSC1, 1};
   return Tile{128, kStoreNT, 1};
 }

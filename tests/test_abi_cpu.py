@@ -255,8 +255,18 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(64, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # GVA: 2048 units, T = 3
     assert L(256, 4, 32, 32, 128, 128) == (128, 1, 1, 1, 2)      # large batch: 8192 units
     assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 2)      # max bandwidth: 32768 units, T = 8
-    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)           # <= 128 units: latency-bound split
-    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)        # T <= 2
+    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)           # <= 64 units: latency-bound split
+    assert L(4, 4, 16, 16, 128, 128) == (32, 1, 0, 1, 1)
+    assert L(8, 2, 16, 16, 128, 128) == (32, 1, 0, 1, 1)         # ... and <= 128 at T = 2
+    assert L(8, 4, 16, 16, 128, 128) == (128, 1, 0, 4, 1)        # <= 128 units: four column groups
+    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 4, 1)        # 129-447 units: four groups at T = 1 ...
+    assert L(12, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... (one from 320)
+    assert L(12, 4, 32, 32, 128, 128) == (128, 1, 0, 2, 1)       # ... else two
+    assert L(16, 8, 16, 16, 128, 128) == (128, 1, 0, 2, 1)
+    assert L(24, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # 513-1023 units
+    assert L(24, 2, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(24, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(12, 8, 16, 64, 128, 128) == (128, 1, 1, 2, 1)
     assert L(32, 1, 32, 32, 128, 128) == (128, 1, 2, 1, 1)
     assert L(64, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)       # T = 1 queue from 2048 units
     assert L(64, 1, 16, 32, 128, 128) == (128, 1, 2, 1, 1)       # ... not with shared q/k heads
@@ -275,7 +285,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(512, 3, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
     assert L(128, 4, 16, 32, 128, 128) == (128, 1, 1, 1, 2)      # shared q/k heads
     assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0, 1, 1)        # T >= 6
+    assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0, 2, 1)        # T >= 6
     assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(64, 8, 32, 32, 128, 128) == (128, 1, 1, 1, 1)
     assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
@@ -297,6 +307,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 1, 1, 1, 1)      # the grid, AUTO cap kept
     assert L(64, 4, 32, 32, 128, 128, schedule=2) == (128, 1, 1, 2, 2)
     assert L(1, 4, 8, 8, 128, 128, schedule=2) == (128, 1, 0, 1, 2)          # the queue takes whole V
+    assert L(8, 4, 16, 16, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: one group
     assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 1, 0, 1, 2)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: the grid
     assert L(3, 16, 1, 4, 64, 64, schedule=2) == (64, 1, 0, 1, 2)
