@@ -8,12 +8,16 @@
 // token's state and conv window written, conv cache rolled in place).
 //
 // Design (our own, for gfx950; the page's CuTe kernels target NVIDIA parts):
-//   * One workgroup (WG) per (sequence n, value head hv, V-tile vt); the WG holds the
-//     fp32 K x VT state tile in VGPRs for all T tokens. Its NW wave64s split K: wave
-//     w owns rows [w*RW, (w+1)*RW). Inside a wave, LPR = VT/4 lanes span a row (one
-//     16-byte vector of 4 columns each) and Q = 64/LPR consecutive rows are covered
-//     by one instruction, so every state load and snapshot store of a wave moves
-//     64 x 16 contiguous bytes (two whole 512-byte rows when VT = 128).
+//   * A unit of work is one (sequence n, value head hv, V-tile vt), done by one
+//     workgroup (WG) that holds the fp32 K x VT state tile in VGPRs for all T tokens.
+//     Two schedules: the grid (one WG per unit) and the queue (as many WGs as are
+//     resident at once, each pulling units from a counter in the workspace until none
+//     are left, so that no XCD idles while another still has units). The WG's NW
+//     wave64s split K: wave w owns rows [w*RW, (w+1)*RW). Inside a wave, LPR = VT/4
+//     lanes span a row (one 16-byte vector of 4 columns each) and Q = 64/LPR
+//     consecutive rows are covered by one instruction, so every state load and
+//     snapshot store of a wave moves 64 x 16 contiguous bytes (two whole 512-byte rows
+//     when VT = 128).
 //   * Prologue: every input the WG needs besides the state (its q/k channels, its
 //     v-column channels, their conv cache and weights, the gate row, dt_bias, beta)
 //     is fetched with 16-byte loads into LDS; the 16-byte state loads are issued
@@ -43,7 +47,6 @@
 #include <string.h>
 
 #include <atomic>
-
 #include <type_traits>
 
 #include "kda_verify.h"
