@@ -220,6 +220,74 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
           f"(worst: H={worst['H']} T={worst['T']} N={worst['N']})", flush=True)
 
 
+def sweep_store(out_path: str) -> None:
+    """Snapshot store policy sweep: on each shape, AUTO's launch (tile, cap, column groups,
+    schedule) with the streaming stores (policy 1) and the device-scope streaming stores
+    (policy 2), timed alternately. Shapes: T = 1..8, 256..32768 (sequence, value head)
+    units, q/k heads shared by 1 or 2 value heads (H = 16, K = V = 128, bf16, softplus),
+    buffers rotated so that >= 1 GiB is touched between reuses. One JSON object per shape."""
+    import torch
+
+    import linear_attention_decode_kda_amd as kda
+    from linear_attention_decode_kda_amd import synth
+
+    dev = torch.device("cuda:0")
+    H = 16
+    with open(out_path, "w") as f:
+        for g in (1, 2):
+            HV = H * g
+            for T in range(1, 9):
+                for units in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+                    N = units // HV
+                    w = synth.Workload("sweep_store", N=N, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16",
+                                       gate="softplus", seed=1)
+                    b_alg = synth.algorithmic_bytes(w)
+                    nset = max(2, min(16, (1 << 30) // b_alg + 1))
+                    sets = []
+                    for _ in range(nset):
+                        inp = {
+                            "mixed_qkv": torch.randn(N, T, w.C, device=dev).to(torch.bfloat16),
+                            "conv_weight": (torch.randn(w.C, 4, device=dev) * 0.5).to(torch.bfloat16),
+                            "conv_state": torch.randn(N, w.C, 3, device=dev).to(torch.bfloat16),
+                            "gate": torch.randn(N, T, HV, 128, device=dev).to(torch.bfloat16),
+                            "A_log": torch.rand(HV, device=dev),
+                            "dt_bias": torch.randn(HV * 128, device=dev) * 0.1,
+                            "beta": torch.randn(N, T, HV, device=dev).to(torch.bfloat16),
+                            "state": torch.randn(N, HV, 128, 128, device=dev) * 0.1,
+                        }
+                        sets.append((inp, kda.alloc_outputs(w, dev)))
+                    launch = kda.select_launch(kda.params_for(w))
+                    calls = {}
+                    for pol in (1, 2):
+                        p = kda.params_for(w, store_policy=pol)
+                        ws = kda.alloc_workspace(p, dev)
+                        calls[pol] = [kda.PreparedVerify(p, a, o, ws) for a, o in sets]
+                    # one rotation over the buffer sets for both policies: consecutive calls never
+                    # share a set, so neither policy reads what the other just left in the cache
+                    for i in range(2 * nset):
+                        for pol in (1, 2):
+                            calls[pol][(2 * i + pol) % nset]()
+                    reps = max(12, 2 * nset)
+                    ev = {pol: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                for _ in range(reps)] for pol in (1, 2)}
+                    for i in range(reps):
+                        for pol in (1, 2):
+                            ev[pol][i][0].record()
+                            calls[pol][(2 * i + pol) % nset]()
+                            ev[pol][i][1].record()
+                    torch.cuda.synchronize()
+                    ms = {pol: sorted(a.elapsed_time(b) for a, b in ev[pol])[reps // 2] for pol in (1, 2)}
+                    pct = {pol: 100 * b_alg / ms[pol] / 1e6 / HBM_PEAK_GBPS for pol in (1, 2)}
+                    row = {"H": H, "HV": HV, "T": T, "N": N, "units": units, "bytes": b_alg, "launch": launch,
+                           "ms": ms, "pct": pct}
+                    f.write(json.dumps(row) + "\n")
+                    f.flush()
+                    print(f"g={g} T={T} units={units:6d} auto_store={launch['store_policy']} "
+                          f"nt {pct[1]:5.1f}%  nt+dev {pct[2]:5.1f}%", flush=True)
+                    del sets, calls
+                    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,7 +301,7 @@ def main():
                     help="verify (the headline), verify on pooled buffers with scattered rows, the accept "
                          "step, or the unfused two-kernel form of verify (same algorithmic bytes)")
     ap.add_argument("--tile", type=int, default=0, help="override: V columns per workgroup (32, 64, 128)")
-    ap.add_argument("--store", type=int, default=0, help="override: snapshot stores, 1 streaming, 2 write-through")
+    ap.add_argument("--store", type=int, default=0, help="override: snapshot stores, 1 streaming, 2 streaming at device scope")
     ap.add_argument("--occ", type=int, default=0, help="override: at most 1, 2, 4 or 6 workgroups per CU (8: no cap)")
     ap.add_argument("--groups", type=int, default=0, help="override: column groups of a whole-V workgroup (1, 2, 4)")
     ap.add_argument("--schedule", type=int, default=0,
@@ -243,6 +311,8 @@ def main():
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
                     help="run the H x T x N sweep over tile widths and store policies instead")
     ap.add_argument("--sweep-quick", action="store_true", help="a reduced sweep grid")
+    ap.add_argument("--sweep-store", default=None, metavar="OUT.jsonl",
+                    help="time AUTO's launch with store policy 1 and 2 over T x units x shared heads")
     ap.add_argument("--sweep-h", default="", help="comma-separated H = HV values for --sweep (default all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
@@ -263,6 +333,9 @@ def main():
 
     if args.sweep:
         sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x])
+        return
+    if args.sweep_store:
+        sweep_store(args.sweep_store)
         return
 
     if args.copy_calibration:

@@ -84,8 +84,8 @@ typedef struct {
    * every tile width and store policy gives the same bits. */
   int32_t tile_columns;     /* V columns per workgroup: 32, 64 or 128 (K = V = 128 only);
                                V selects LARGE, fewer SMALL, and overrides `variant` */
-  int32_t store_policy;     /* snapshot stores: 1 streaming (non-temporal), 2 write-through
-                               at device scope */
+  int32_t store_policy;     /* snapshot stores: 1 streaming (non-temporal hint), 2 streaming
+                               at device scope (non-temporal hint with device coherence) */
   int32_t max_wg_per_cu;    /* at most 1, 2, 4 or 6 workgroups per compute unit, by reserving
                                LDS per workgroup (fewer concurrent snapshot streams can use
                                HBM better); the kernel's own limits still apply. 8: no cap.
@@ -132,7 +132,8 @@ kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream
 int32_t kda_select_variant(const kda_verify_params* p);
 
 /* The launch configuration kda_conv_verify_decode would use for these params (after the
- * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 write-through),
+ * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 streaming at
+ * device scope),
  * workgroups-per-CU cap (0 = none), column groups per workgroup and schedule (1 grid,
  * 2 queue). Host-only; any output pointer may be NULL. Returns the params' validation
  * status (outputs untouched unless KDA_OK). */

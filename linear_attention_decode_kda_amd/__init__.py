@@ -150,7 +150,7 @@ def select_variant(p: Params) -> int:
 
 def select_launch(p: Params) -> Dict[str, int]:
     """The launch configuration the library picks for ``p``: tile_columns, store_policy
-    (1 streaming, 2 write-through), max_wg_per_cu (0 = no cap), column_groups and schedule
+    (1 streaming, 2 streaming at device scope), max_wg_per_cu (0 = no cap), column_groups and schedule
     (1 grid, 2 queue)."""
     t, s, o, g, q = (ctypes.c_int32() for _ in range(5))
     st = load().kda_select_launch(ctypes.byref(p), ctypes.byref(t), ctypes.byref(s), ctypes.byref(o),

@@ -132,14 +132,16 @@ __device__ __forceinline__ float lane_sum_from(float x) {
   return x;
 }
 
-// One 16-byte snapshot store with the chosen cache policy (vector memory only). The
-// write-through form is inline assembly, which the compiler's hazard tracking cannot see
-// as a store: a 16-byte store's data registers must not be overwritten by VALU for two
-// wait states after it on gfx950, so the statement supplies them itself (s_nop 1).
+// One 16-byte snapshot store with the chosen cache policy (vector memory only): the
+// streaming (non-temporal) hint alone, or the streaming hint at device scope (nt sc1),
+// which MI355X sweeps found faster on the large grids (see kStoreNTDev). The device-scope
+// form is inline assembly, which the compiler's hazard tracking cannot see as a store: a
+// 16-byte store's data registers must not be overwritten by VALU for two wait states after
+// it on gfx950, so the statement supplies them itself (s_nop 1).
 template <int STP>
 __device__ __forceinline__ void store_snapshot(float* p, f32x4 v) {
   if constexpr (STP == 1)
-    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
   else
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
@@ -181,8 +183,11 @@ struct Args {
   float lower_bound, softplus_beta, softplus_threshold, scale, eps;
 };
 
-// Snapshot store cache policy: streaming (nt) or agent-coherent write-through (sc1).
-enum StorePolicy { kStoreNT = 0, kStoreSC1 = 1 };
+// Snapshot store cache policy: the streaming hint (nt), or the streaming hint with device
+// scope (nt sc1). Timed on MI355X against plain device-scope stores (sc1) and system scope
+// (nt sc0 sc1): nt sc1 moved large_batch from 80.3 % (nt) and 76.9 % (sc1) to 82.1 % of
+// peak, and max_bandwidth from 80.8 % (sc1) to 82.7 %; system scope measured the same.
+enum StorePolicy { kStoreNT = 0, kStoreNTDev = 1 };
 
 // Partial-sum plan. A wave's P canonical partial sums of each column are paired in a
 // fixed order of their index bits (1, 2, 0, then 3 when P = 16), the same for every tile
@@ -933,54 +938,72 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
                          dim3(CF::NTHR), args, dyn, stream);
 }
 
-// Tile shape, store policy, workgroups-per-CU cap, column groups and schedule, from sweeps
-// on MI355X (K = V = 128, bf16; every combination timed on each shape, buffers rotated so
-// that each run reads and writes HBM): H = HV x T x N over 200 shapes, GVA shapes (HV = 2H,
-// 4H), column groups on 179 shapes of 1024-32768 units, and the queue schedule against the
-// grid on 105 shapes of 2048-32768 units. The choice per bucket is the one with the best
-// mean. A cap limits how many workgroups stream snapshots at once: from a thousand units
-// up, one whole-V workgroup per CU keeps HBM busiest. From a few thousand units the queue
-// schedule (one resident workgroup per CU pulling units) beats launching a workgroup per
-// unit by 2-14 %: the XCDs no longer finish their fixed shares at different times, and no
+// Tile shape, workgroups-per-CU cap, column groups and schedule, from sweeps on MI355X
+// (K = V = 128, bf16; every combination timed on each shape, buffers rotated so that each
+// run reads and writes HBM): H = HV x T x N over 200 shapes, GVA shapes (HV = 2H, 4H),
+// column groups on 179 shapes of 1024-32768 units, and the queue schedule against the grid
+// on 105 shapes of 2048-32768 units. The choice per bucket is the one with the best mean.
+// A cap limits how many workgroups stream snapshots at once: from a thousand units up, one
+// whole-V workgroup per CU keeps HBM busiest. From a few thousand units the queue schedule
+// (one resident workgroup per CU pulling units) beats launching a workgroup per unit by
+// 2-14 %: the XCDs no longer finish their fixed shares at different times, and no
 // workgroup launch sits between two units of a CU. Below that the queue's first round is
 // most of the work and its counter traffic does not pay.
 //   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
 //     groups; T >= 2 from 4096 units (T = 3 without shared heads from 8192): two column
-//     groups at T = 2 (and T = 3 below 8192), else one; write-through stores at T = 3-4
-//     from 32768 units, T = 6-7 from 16384, T >= 8 from 16384 or with shared q/k heads;
+//     groups at T = 2 (and T = 3 below 8192), else one;
 //   otherwise the grid. Below 1024 units (a sweep of 100 shapes of 128-768 units, T = 1-8,
 //     three timings each), where one generation of workgroups is most of the call and
 //     shorter per-unit chains pay:
 //     <= 64 units, and <= 128 at T = 2: the 32-column split (4 WGs per unit);
 //     <= 128 units: whole V in four column groups; 129-447: whole V in two column groups
-//     (T = 1: four below 320 units, else one); 448-512: whole V, write-through at T >= 6;
-//     513-1023: whole V at T = 1, write-through at T = 2, else one WG per CU in two groups;
+//     (T = 1: four below 320 units, else one); 448-512: whole V;
+//     513-1023: whole V at T <= 2, else one WG per CU in two groups;
 //   from 1024 units, whole V: T <= 2: two WGs per CU (64 columns at T = 2 from 2048);
-//     T <= 5: one WG per CU in two column groups; T >= 6: one WG per CU: shared q/k heads
-//     in two column groups below 2048 units and write-through above, otherwise streaming.
+//     T <= 5: one WG per CU in two column groups; T >= 6: one WG per CU, with shared q/k
+//     heads in two column groups below 2048 units.
 // Every tile width, grouping and schedule uses the same K split (32 rows per wave) and the
 // same partial-sum tree, so all of them return bit-identical results; the cap and the
 // schedule only change which CU runs a unit, and when.
-Tile auto_tile_128(long long units, int T, int g) {
+Tile auto_shape_128(long long units, int T, int g) {
   // queue schedule, one whole-V workgroup per CU
   if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
   if (T >= 2 && units >= 4096 && !(T == 3 && g == 1 && units < 8192)) {
     if (T == 2 || (T == 3 && units < 8192)) return Tile{128, kStoreNT, 1, 2, true};
-    if (T <= 5) return Tile{128, T <= 4 && units >= 32768 ? kStoreSC1 : kStoreNT, 1, 1, true};
-    if (T <= 7) return Tile{128, units >= 16384 ? kStoreSC1 : kStoreNT, 1, 1, true};
-    return Tile{128, g == 1 && units < 16384 ? kStoreNT : kStoreSC1, 1, 1, true};
+    return Tile{128, kStoreNT, 1, 1, true};
   }
   // the grid: below 1024 units
   if (units <= 64 || (units <= 128 && T == 2)) return Tile{32, kStoreNT};
   if (units <= 128) return Tile{128, kStoreNT, 0, 4};
   if (units < 448) return Tile{128, kStoreNT, 0, T > 1 ? 2 : units < 320 ? 4 : 1};
-  if (units <= 512) return Tile{128, T >= 6 ? kStoreSC1 : kStoreNT};
-  if (units < 1024) return T == 1 ? Tile{128, kStoreNT} : T == 2 ? Tile{128, kStoreSC1} : Tile{128, kStoreNT, 1, 2};
+  if (units <= 512) return Tile{128, kStoreNT};
+  if (units < 1024) return T <= 2 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 1, 2};
   // the grid from 1024 units
   if (T <= 2) return T == 2 && units >= 2048 ? Tile{64, kStoreNT, 2} : Tile{128, kStoreNT, 2};
   if (T <= 5) return Tile{128, kStoreNT, 1, 2};
-  if (g > 1) return units < 2048 ? Tile{128, kStoreNT, 1, 2} : Tile{128, kStoreSC1, 1};
+  if (g > 1 && units < 2048) return Tile{128, kStoreNT, 1, 2};
   return Tile{128, kStoreNT, 1};
+}
+
+// Snapshot store policy for AUTO's launch, from a sweep that timed AUTO's launch with both
+// policies on 128 shapes (T = 1-8, 256-32768 units, q/k heads shared by 1 or 2 value
+// heads; H = 16), the two alternating over distinct buffer sets so that neither reads what
+// the other left in the last-level cache. The device-scope streaming stores win by 1-8
+// points of HBM peak from 8192 units (T >= 2; T = 1 only from 16384 without shared q/k
+// heads), from 4096 units at T >= 4, and at T >= 6 on grids of 512-4095 units (512-1023
+// with shared heads); elsewhere the two are within noise or the plain streaming stores win.
+int auto_store_128(long long units, int T, int g) {
+  if (T == 1) return g == 1 && units >= 16384 ? kStoreNTDev : kStoreNT;
+  if (units >= 8192) return kStoreNTDev;
+  if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
+  if (T >= 6 && units >= 512 && (g == 1 || units < 1024)) return kStoreNTDev;
+  return kStoreNT;
+}
+
+Tile auto_tile_128(long long units, int T, int g) {
+  Tile t = auto_shape_128(units, T, g);
+  t.stp = auto_store_128(units, T, g);
+  return t;
 }
 
 // The AUTO choice with the caller's overrides applied. A cap belongs to the AUTO tile: when
@@ -1005,7 +1028,7 @@ Tile choose_tile(const kda_verify_params* p) {
       t.vt = 32;
     else if (p->schedule == 2)
       t.vt = 128;  // the queue runs whole-V workgroups
-    if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreSC1 : kStoreNT;
+    if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreNTDev : kStoreNT;
     // fp32 inputs at T > 8: a whole-V workgroup's staged inputs and conv windows would not
     // fit in LDS; two 64-column workgroups give the same bits
     if (p->in_dtype == KDA_F32 && p->T > 8 && t.vt == 128) {
@@ -1030,22 +1053,22 @@ LaunchFn pick_tmax(int K, int V, Tile tl) {
     constexpr bool whole_v = !(sizeof(R) == 4 && TMAX > 8 && PRE == 0);
     if constexpr (whole_v) {
       if (tl.vt == 128 && tl.g == 4)
-        return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreSC1, PRE, 4>, R>
+        return tl.stp == kStoreNTDev ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNTDev, PRE, 4>, R>
                                    : &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNT, PRE, 4>, R>;
       if (tl.vt == 128 && tl.g == 2)
-        return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1, PRE, 2>, R>
+        return tl.stp == kStoreNTDev ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNTDev, PRE, 2>, R>
                                    : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT, PRE, 2>, R>;
       if (tl.vt == 128)
-        return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreSC1, PRE>, R>
+        return tl.stp == kStoreNTDev ? &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNTDev, PRE>, R>
                                    : &launch<Cfg<R, 128, 128, 128, 4, TMAX, kStoreNT, PRE>, R>;
     } else {
       if (tl.vt == 128) return nullptr;
     }
     if (tl.g != 1) return nullptr;
     if (tl.vt == 64)
-      return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreSC1, PRE>, R>
+      return tl.stp == kStoreNTDev ? &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNTDev, PRE>, R>
                                  : &launch<Cfg<R, 128, 128, 64, 4, TMAX, kStoreNT, PRE>, R>;
-    return tl.stp == kStoreSC1 ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreSC1, PRE>, R>
+    return tl.stp == kStoreNTDev ? &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNTDev, PRE>, R>
                                : &launch<Cfg<R, 128, 128, 32, 4, TMAX, kStoreNT, PRE>, R>;
   }
   if (K == 64 && V == 64) {
@@ -1176,7 +1199,7 @@ kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, 
   if (st != KDA_OK) return st;
   const Tile t = choose_tile(p);
   if (tile_columns) *tile_columns = t.vt;
-  if (store_policy) *store_policy = t.stp == kStoreSC1 ? 2 : 1;
+  if (store_policy) *store_policy = t.stp == kStoreNTDev ? 2 : 1;
   if (max_wg_per_cu) *max_wg_per_cu = t.occ;
   if (column_groups) *column_groups = t.g;
   if (schedule) *schedule = t.queue ? 2 : 1;

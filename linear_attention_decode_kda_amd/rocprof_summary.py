@@ -4,6 +4,7 @@
   python -m linear_attention_decode_kda_amd.rocprof_summary traffic <workload> <variant>
          <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <cmd-file> <out.json>
   python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md <sweep.jsonl> <cmd> <out.md>
+  python -m linear_attention_decode_kda_amd.rocprof_summary store-md <sweep_store.jsonl> <cmd> <out.md>
 
 `traffic` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the verify
 kernel by what the same counters read for a plain 1 GiB device copy (read 1 GiB, write
@@ -44,6 +45,34 @@ def stats(csv_path: str, cmd: str, out: str) -> None:
         short = name if len(name) < 110 else name[:107] + "..."
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def store_md(jsonl: str, cmd: str, out: str) -> None:
+    """Table of the store-policy sweep (bench.py --sweep-store) with the policy the library's
+    AUTO rule picks for each shape now (host-only call, no GPU)."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import linear_attention_decode_kda_amd as kda
+
+    rows = [json.loads(l) for l in open(jsonl) if l.strip()]
+    lines = ["# Snapshot store policy sweep (K = V = 128, bf16, softplus gate, H = 16)", "",
+             f"Command: `{cmd}`", "",
+             "AUTO's launch (tile, cap, column groups, schedule) timed with the streaming stores (1: `nt`) and "
+             "the streaming stores at device scope (2: `nt sc1`), alternately over distinct buffer sets (>= 1 GiB "
+             "touched between reuses of a set); median of >= 12 calls each. Percent of the 8 TB/s HBM peak = "
+             "algorithmic bytes / kernel time. `AUTO` is the policy the library picks for the shape.", "",
+             "| value heads per q/k head | T | units | 1: nt % | 2: nt sc1 % | AUTO |", "|---|---|---|---|---|---|"]
+    gain = []
+    for r in rows:
+        g = r["HV"] // r["H"]
+        p = kda.make_params(r["N"], r["T"], r["H"], r["HV"], 128, 128)
+        auto = kda.select_launch(p)["store_policy"]
+        p1, p2 = r["pct"]["1"], r["pct"]["2"]
+        gain.append((max(p1, p2) - (p1 if auto == 1 else p2)))
+        lines.append(f"| {g} | {r['T']} | {r['units']} | {p1:.1f} | {p2:.1f} | {auto} |")
+    lines += ["", f"AUTO's pick is within {max(gain):.1f} points of the faster policy on every shape "
+              f"(mean {statistics.mean(gain):.2f} points)."]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -135,5 +164,7 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:10])
     elif sys.argv[1] == "sweep-md":
         sweep_md(*sys.argv[2:5])
+    elif sys.argv[1] == "store-md":
+        store_md(*sys.argv[2:5])
     else:
         raise SystemExit(__doc__)

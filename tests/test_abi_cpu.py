@@ -253,7 +253,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0, 1, 1)            # tiny: the only K = V = 16 tile
     assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0, 1, 1)       # small batch: 512 units, T = 4
     assert L(64, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # GVA: 2048 units, T = 3
-    assert L(256, 4, 32, 32, 128, 128) == (128, 1, 1, 1, 2)      # large batch: 8192 units
+    assert L(256, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)      # large batch: 8192 units
     assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 2)      # max bandwidth: 32768 units, T = 8
     assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)           # <= 64 units: latency-bound split
     assert L(4, 4, 16, 16, 128, 128) == (32, 1, 0, 1, 1)
@@ -264,38 +264,50 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(12, 4, 32, 32, 128, 128) == (128, 1, 0, 2, 1)       # ... else two
     assert L(16, 8, 16, 16, 128, 128) == (128, 1, 0, 2, 1)
     assert L(24, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # 513-1023 units
-    assert L(24, 2, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(24, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)
     assert L(24, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(12, 8, 16, 64, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(12, 8, 16, 64, 128, 128) == (128, 2, 1, 2, 1)
     assert L(32, 1, 32, 32, 128, 128) == (128, 1, 2, 1, 1)
     assert L(64, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)       # T = 1 queue from 2048 units
     assert L(64, 1, 16, 32, 128, 128) == (128, 1, 2, 1, 1)       # ... not with shared q/k heads
-    assert L(512, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)
+    assert L(512, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
     assert L(64, 2, 32, 32, 128, 128) == (64, 1, 2, 1, 1)
     assert L(128, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2 queue from 4096 units
-    assert L(512, 2, 64, 64, 128, 128) == (128, 1, 1, 2, 2)
+    assert L(512, 2, 64, 64, 128, 128) == (128, 2, 1, 2, 2)
     assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T <= 5
     assert L(32, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(128, 4, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(128, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T = 3: the grid below 8192 ...
-    assert L(256, 3, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(256, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 2)      # ... unless q/k heads are shared
-    assert L(512, 3, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
-    assert L(128, 4, 16, 32, 128, 128) == (128, 1, 1, 1, 2)      # shared q/k heads
+    assert L(512, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(128, 4, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # shared q/k heads
     assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
     assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0, 2, 1)        # T >= 6
     assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
-    assert L(64, 8, 32, 32, 128, 128) == (128, 1, 1, 1, 1)
+    assert L(64, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
-    assert L(128, 8, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(64, 8, 16, 32, 128, 128) == (128, 1, 1, 1, 1)
+    assert L(128, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(256, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(256, 6, 32, 32, 128, 128) == (128, 1, 1, 1, 2)
+    assert L(256, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(512, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    # the edges of the store rule (2: streaming at device scope)
+    assert L(511, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)      # T = 1: from 16384 units, no sharing
+    assert L(512, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
+    assert L(255, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2: from 8192 units
+    assert L(256, 2, 32, 32, 128, 128) == (128, 2, 1, 2, 2)
+    assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T >= 4: from 4096 units
+    assert L(128, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(15, 6, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T >= 6: from 512 units ...
+    assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(127, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
+    assert L(16, 6, 16, 32, 128, 128) == (128, 2, 0, 1, 1)       # ... with shared q/k heads below 1024
+    assert L(32, 6, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6, 1, 1)
-    assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 1, 0, 1, 1)   # the AUTO cap goes with its tile
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 2, 0, 1, 1)   # the AUTO cap goes with its tile
     assert L(64, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: no AUTO cap
     assert L(64, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0, 2, 1)   # 8: explicitly none
     assert L(64, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2, 1, 1)
@@ -304,12 +316,12 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(64, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1, 2, 1)
     assert L(64, 4, 32, 32, 128, 128, column_groups=4) == (128, 1, 1, 4, 1)
     assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2, 1, 1)
-    assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 1, 1, 1, 1)      # the grid, AUTO cap kept
+    assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 2, 1, 1, 1)      # the grid, AUTO cap kept
     assert L(64, 4, 32, 32, 128, 128, schedule=2) == (128, 1, 1, 2, 2)
     assert L(1, 4, 8, 8, 128, 128, schedule=2) == (128, 1, 0, 1, 2)          # the queue takes whole V
     assert L(8, 4, 16, 16, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: one group
-    assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 1, 0, 1, 2)
-    assert L(256, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: the grid
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 2, 0, 1, 2)
+    assert L(256, 4, 32, 32, 128, 128, tile_columns=128) == (128, 2, 0, 1, 1)  # caller's tile: the grid
     assert L(3, 16, 1, 4, 64, 64, schedule=2) == (64, 1, 0, 1, 2)
     # fp32 at T > 8: two 64-column workgroups, one group each, on the grid
     assert L(64, 9, 8, 16, 128, 128, dtype="f32") == (64, 1, 1, 1, 1)

@@ -231,9 +231,9 @@ def test_zero_q_k_channels():
     assert torch.count_nonzero(got["o"]) == 0
 
 
-@pytest.mark.parametrize("w", [W(64, 2, 64, 64, 128, 128, gate="safe"),   # 4096 units, streaming stores
-                               W(16, 4, 8, 16, 128, 128),                  # 256 units, write-through stores
-                               W(32, 8, 16, 32, 128, 128, gate="safe")])   # T = 8, write-through stores
+@pytest.mark.parametrize("w", [W(64, 4, 16, 32, 128, 128, gate="safe"),   # 2048 units at T = 4, streaming stores
+                               W(16, 4, 8, 16, 128, 128),                  # 256 units, device-scope streaming stores
+                               W(32, 8, 16, 32, 128, 128, gate="safe")])   # T = 8, shared q/k heads, 1024 units: streaming
 def test_every_tile_shape_bit_identical(w):
     """SMALL (32-column WGs) and LARGE (whole-V WGs) with the store policy dispatch picks for
     the shape give the same bits; a sample of sequences is also checked against the oracle."""
@@ -254,7 +254,7 @@ def test_explicit_tile_and_store_overrides_bit_identical(w):
     """Every tile width (32, 64, 128 columns per WG), both snapshot store policies, the
     workgroups-per-CU caps and both schedules give the same bits, for each token-count
     template; one of them
-    is checked against the oracle. (The write-through store is inline assembly: a missing
+    is checked against the oracle. (The device-scope store is inline assembly: a missing
     wait after it once let later VALU writes reach memory in place of the snapshot.)"""
     inp = synth.make_inputs(w)
     outs = []
