@@ -164,9 +164,12 @@ def test_commit_matches_oracle_and_prefix_verify(w):
         assert torch.equal(d["conv_state"][idx["conv_state_indices"][n].item()], one["conv_state"][0]), n
 
 
-def test_serving_loop_verify_commit_chain():
+@pytest.mark.parametrize("launch", [dict(), dict(store_policy=2), dict(store_policy=2, schedule=2, max_wg_per_cu=1)],
+                         ids=["auto", "device-scope-stores", "device-scope-stores-queue"])
+def test_serving_loop_verify_commit_chain(launch):
     """Three rounds of verify -> commit on shared pools; each round's outputs match the
-    oracle run on the pools the previous rounds left."""
+    oracle run on the pools the previous rounds left. Also with the snapshots streamed at
+    device scope (on the grid and the queue): the commit and the next verify read them."""
     w = W(4, 4, 2, 4, gate="safe")
     slots = (6, 6, 5)
     pinp, idx, init = _pooled_case(w, slots, seed=11)
@@ -174,7 +177,7 @@ def test_serving_loop_verify_commit_chain():
     d = {k: v.cuda() for k, v in pinp.items()}
     di = {k: v.cuda() for k, v in idx.items()}
     out = {k: v.cuda() for k, v in init.items()}
-    p = kda.params_for(w)
+    p = kda.params_for(w, **launch)
     pools = kda.make_pools(w.N, di["conv_state_indices"], di["cache_indices"], di["intermediate_state_indices"],
                            *slots)
     ws = kda.alloc_workspace(p)
