@@ -33,3 +33,16 @@ def test_host_threads_bounds(monkeypatch):
     assert bench.host_threads() == 3
     monkeypatch.setenv("OMP_NUM_THREADS", "junk")
     assert 1 <= bench.host_threads() <= 16
+
+
+def test_timeline_instrumentation_applies_to_the_kernel_source():
+    """The timeline tool patches the current kernel source (sixteen stamps per unit); a
+    kernel edit that moves one of its anchors must fail here, not on the GPU."""
+    from linear_attention_decode_kda_amd import build as b
+    from linear_attention_decode_kda_amd import timeline
+
+    with open(b.SRC) as f:
+        src = timeline._instrument(f.read())
+    for q in range(15):
+        assert f"st_[{q}]" in src, q
+    assert "kda_timeline_set_stamps" in src and "a.stamps = g_stamps;" in src
