@@ -15,6 +15,7 @@ durations, and per-XCD end times and unit durations.
 
   python -m linear_attention_decode_kda_amd.timeline build
   python -m linear_attention_decode_kda_amd.timeline run small_batch gva large_batch > out.md
+  python -m linear_attention_decode_kda_amd.timeline run gva gva:schedule=2,max_wg_per_cu=1,tile_columns=128
 """
 from __future__ import annotations
 
@@ -115,9 +116,12 @@ def run(names) -> None:
           " | ".join(NAMES[1:]) + " |")
     print("|---" * (4 + len(NAMES) - 1) + "|")
     per_xcd = []
-    for name in names:
+    for spec in names:
+        # "workload" or "workload:key=value,..." with params overrides (schedule=2, ...)
+        name, _, over = spec.partition(":")
+        kw = {k: int(v) for k, v in (x.split("=") for x in over.split(",") if x)}
         w = synth.WORKLOADS[name]
-        p = kda.params_for(w)
+        p = kda.params_for(w, **kw)
         la = kda.select_launch(p)
         nwg = w.N * w.HV * (128 // la["tile_columns"])
         inp = {k: v.to(dev) for k, v in synth.make_inputs(w).items()}
@@ -160,8 +164,8 @@ def run(names) -> None:
             vals = [ph[c] for ph in phases if c in ph]
             cells.append(f"{np.median(vals):.2f}" if vals else "-")
         spread = f"{np.median(spreads):.1f}" if max(spreads) > 0 else "-"
-        print(f"| {name} | {launch} | {np.median(spans):.1f} | {spread} | " + " | ".join(cells) + " |")
-        per_xcd.append((name, xcd))
+        print(f"| {spec} | {launch} | {np.median(spans):.1f} | {spread} | " + " | ".join(cells) + " |")
+        per_xcd.append((spec, xcd))
         del inp, out, st
         torch.cuda.empty_cache()
     print("\nPer XCD (median over the five calls): last unit end (us) / median unit duration (us) / units\n")
