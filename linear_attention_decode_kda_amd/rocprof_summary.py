@@ -131,8 +131,8 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
              "between reuses; median of >= 8 calls per combination), summarised by "
              f"`python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md {os.path.basename(jsonl)} ...`.",
              "",
-             "Combinations are tile/store[/cap][ gN][ q]: V columns per workgroup, snapshot stores (1 "
-             "streaming, 2 write-through), the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed "
+             "Combinations are tile/store[/cap][ gN][ q]: V columns per workgroup, snapshot store policy "
+             "(1 streaming, 2 the library's policy 2 at the time of the run), the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed "
              "only where the grid has more workgroups than it lets run at once), column groups of a "
              "whole-V workgroup (gN), and q for the queue schedule (resident workgroups pulling units; "
              "otherwise one workgroup per unit). Percent of the 8 TB/s HBM "
