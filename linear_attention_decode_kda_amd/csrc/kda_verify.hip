@@ -954,8 +954,9 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 // workgroup launch sits between two units of a CU. Below that the queue's first round is
 // most of the work and its counter traffic does not pay.
 //   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
-//     groups; T >= 2 from 4096 units (T = 3 without shared heads from 8192): two column
-//     groups at T = 2 (and T = 3 below 8192), else one;
+//     groups; T >= 2 from 4096 units (T = 3 without shared heads from 8192, T = 2 without
+//     shared heads from 2048: a refreshed H = HV sweep, +1.4-5.6 %): two column groups at
+//     T = 2 (and T = 3 below 8192), else one;
 //   otherwise the grid. Below 1024 units (a sweep of 100 shapes of 128-768 units, T = 1-8,
 //     three timings each), where one generation of workgroups is most of the call and
 //     shorter per-unit chains pay:
@@ -972,7 +973,7 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 Tile auto_shape_128(long long units, int T, int g) {
   // queue schedule, one whole-V workgroup per CU
   if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
-  if (T >= 2 && units >= 4096 && !(T == 3 && g == 1 && units < 8192)) {
+  if ((T >= 2 && units >= 4096 && !(T == 3 && g == 1 && units < 8192)) || (T == 2 && g == 1 && units >= 2048)) {
     if (T == 2 || (T == 3 && units < 8192)) return Tile{128, kStoreNT, 1, 2, true};
     return Tile{128, kStoreNT, 1, 1, true};
   }
@@ -992,14 +993,17 @@ Tile auto_shape_128(long long units, int T, int g) {
 // Snapshot store policy for AUTO's launch, from a sweep that timed AUTO's launch with both
 // policies on 128 shapes (T = 1-8, 256-32768 units, q/k heads shared by 1 or 2 value
 // heads; H = 16), the two alternating over distinct buffer sets so that neither reads what
-// the other left in the last-level cache. The device-scope streaming stores win by 1-8
-// points of HBM peak from 8192 units (T >= 2; T = 1 only from 16384 without shared q/k
-// heads), from 4096 units at T >= 4, and at T >= 6 on grids of 512-4095 units (512-1023
-// with shared heads); elsewhere the two are within noise or the plain streaming stores win.
+// the other left in the last-level cache, and a refreshed H = HV sweep of every launch
+// combination. The device-scope streaming stores win by 1-8 points of HBM peak from 8192
+// units at T >= 2, from 4096 units at T >= 4, at T = 1 from 1024 units (below 8192 with
+// shared q/k heads), at T = 2 on 1024-2047 units, and at T >= 6 on grids of 512-4095 units
+// (512-1023 with shared heads); elsewhere the two are within noise or the plain streaming
+// stores win.
 int auto_store_128(long long units, int T, int g) {
-  if (T == 1) return g == 1 && units >= 16384 ? kStoreNTDev : kStoreNT;
+  if (T == 1) return units >= 1024 && (g == 1 || units < 8192) ? kStoreNTDev : kStoreNT;
   if (units >= 8192) return kStoreNTDev;
   if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
+  if (T == 2 && units >= 1024 && units < 2048) return kStoreNTDev;
   if (T >= 6 && units >= 512 && (g == 1 || units < 1024)) return kStoreNTDev;
   return kStoreNT;
 }

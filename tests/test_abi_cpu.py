@@ -267,11 +267,11 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(24, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)
     assert L(24, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(12, 8, 16, 64, 128, 128) == (128, 2, 1, 2, 1)
-    assert L(32, 1, 32, 32, 128, 128) == (128, 1, 2, 1, 1)
-    assert L(64, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)       # T = 1 queue from 2048 units
-    assert L(64, 1, 16, 32, 128, 128) == (128, 1, 2, 1, 1)       # ... not with shared q/k heads
+    assert L(32, 1, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
+    assert L(64, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)       # T = 1 queue from 2048 units
+    assert L(64, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)       # ... not with shared q/k heads
     assert L(512, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
-    assert L(64, 2, 32, 32, 128, 128) == (64, 1, 2, 1, 1)
+    assert L(64, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)
     assert L(128, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2 queue from 4096 units
     assert L(512, 2, 64, 64, 128, 128) == (128, 2, 1, 2, 2)
     assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T <= 5
@@ -295,8 +295,16 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(256, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(512, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     # the edges of the store rule (2: streaming at device scope)
-    assert L(511, 1, 32, 32, 128, 128) == (128, 1, 1, 4, 2)      # T = 1: from 16384 units, no sharing
-    assert L(512, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
+    assert L(31, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 1: from 1024 units ...
+    assert L(32, 1, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
+    assert L(511, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
+    assert L(255, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)      # ... with shared q/k heads below 8192
+    assert L(256, 1, 16, 32, 128, 128) == (128, 1, 2, 1, 1)
+    assert L(31, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 2: 1024-2047 units
+    assert L(32, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
+    assert L(63, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
+    assert L(64, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)       # T = 2 queue from 2048 units, no sharing
+    assert L(64, 2, 16, 32, 128, 128) == (64, 1, 2, 1, 1)        # ... the grid with shared q/k heads
     assert L(255, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2: from 8192 units
     assert L(256, 2, 32, 32, 128, 128) == (128, 2, 1, 2, 2)
     assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T >= 4: from 4096 units
