@@ -139,14 +139,15 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
     }
 
 
-def sweep(out_path: str, quick: bool = False, hs=None) -> None:
+def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1) -> None:
     """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
     cap on the grid schedule, and the queue schedule of whole-V workgroups at one per CU in
     1, 2 or 4 column groups (K = V = 128, bf16, softplus). Buffer sets are rotated so that
     at least 1 GiB is touched between reuses (small shapes would otherwise run from the
     256 MB last-level cache). A cap is timed only where the grid has more workgroups than
-    the cap lets run at once, the queue only where there are more units than CUs. Writes
-    one JSON object per shape to out_path and prints a summary line."""
+    the cap lets run at once, the queue only where there are more units than CUs.
+    heads_per_qk > 1 gives each q/k head that many value heads (HV = heads_per_qk H). Writes one JSON object per shape to
+    out_path and prints a summary line."""
     import torch
 
     import linear_attention_decode_kda_amd as kda
@@ -163,7 +164,8 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
         for H in Hs:
             for T in Ts:
                 for N in Ns:
-                    w = synth.Workload(f"sweep", N=N, T=T, H=H, HV=H, K=128, V=128, dtype="bf16",
+                    HV = heads_per_qk * H
+                    w = synth.Workload(f"sweep", N=N, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16",
                                        gate="softplus", seed=1)
                     b_alg = synth.algorithmic_bytes(w)
                     nset = max(1, min(16, (1 << 30) // b_alg + 1))
@@ -173,16 +175,16 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
                             "mixed_qkv": torch.randn(N, T, w.C, device=dev).to(torch.bfloat16),
                             "conv_weight": (torch.randn(w.C, 4, device=dev) * 0.5).to(torch.bfloat16),
                             "conv_state": torch.randn(N, w.C, 3, device=dev).to(torch.bfloat16),
-                            "gate": torch.randn(N, T, H, 128, device=dev).to(torch.bfloat16),
-                            "A_log": torch.rand(H, device=dev),
-                            "dt_bias": torch.randn(H * 128, device=dev) * 0.1,
-                            "beta": torch.randn(N, T, H, device=dev).to(torch.bfloat16),
-                            "state": torch.randn(N, H, 128, 128, device=dev) * 0.1,
+                            "gate": torch.randn(N, T, HV, 128, device=dev).to(torch.bfloat16),
+                            "A_log": torch.rand(HV, device=dev),
+                            "dt_bias": torch.randn(HV * 128, device=dev) * 0.1,
+                            "beta": torch.randn(N, T, HV, device=dev).to(torch.bfloat16),
+                            "state": torch.randn(N, HV, 128, 128, device=dev) * 0.1,
                         }
                         sets.append((inp, kda.alloc_outputs(w, dev)))
                     res = {}
                     for tile, pol, occ, g, sched in combos + [(0, 0, 0, 0, 0)]:
-                        if tile and occ < 8 and N * H * (128 // tile) <= 256 * occ:
+                        if tile and occ < 8 and N * HV * (128 // tile) <= 256 * occ:
                             continue  # the cap would not bind, or no unit would come from the queue
                         p = kda.params_for(w, tile_columns=tile, store_policy=pol, max_wg_per_cu=occ,
                                            column_groups=g, schedule=sched)
@@ -204,14 +206,14 @@ def sweep(out_path: str, quick: bool = False, hs=None) -> None:
                         res[key if tile else "auto"] = ms[len(ms) // 2]
                     best = min((v, k) for k, v in res.items() if k != "auto")
                     auto_p = kda.params_for(w)
-                    row = {"H": H, "T": T, "N": N, "units": N * H, "bytes": b_alg, "ms": res,
+                    row = {"H": H, "HV": HV, "T": T, "N": N, "units": N * HV, "bytes": b_alg, "ms": res,
                            "best": best[1], "best_pct": 100 * b_alg / best[0] / 1e6 / HBM_PEAK_GBPS,
                            "auto_variant": kda.select_variant(auto_p),
                            "auto_over_best": res["auto"] / best[0]}
                     rows.append(row)
                     f.write(json.dumps(row) + "\n")
                     f.flush()
-                    print(f"H={H:3d} T={T} N={N:4d} units={N * H:6d} best={best[1]:7s} "
+                    print(f"H={H:3d} HV={HV:3d} T={T} N={N:4d} units={N * HV:6d} best={best[1]:7s} "
                           f"{row['best_pct']:5.1f}% auto/best={row['auto_over_best']:.3f}", flush=True)
                     del sets
                     torch.cuda.empty_cache()
@@ -313,7 +315,8 @@ def main():
     ap.add_argument("--sweep-quick", action="store_true", help="a reduced sweep grid")
     ap.add_argument("--sweep-store", default=None, metavar="OUT.jsonl",
                     help="time AUTO's launch with store policy 1 and 2 over T x units x shared heads")
-    ap.add_argument("--sweep-h", default="", help="comma-separated H = HV values for --sweep (default all)")
+    ap.add_argument("--sweep-h", default="", help="comma-separated H values for --sweep (default all)")
+    ap.add_argument("--sweep-g", type=int, default=1, help="value heads per q/k head for --sweep (HV = g H)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -332,7 +335,7 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.sweep:
-        sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x])
+        sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x], args.sweep_g)
         return
     if args.sweep_store:
         sweep_store(args.sweep_store)

@@ -993,18 +993,18 @@ Tile auto_shape_128(long long units, int T, int g) {
 // Snapshot store policy for AUTO's launch, from a sweep that timed AUTO's launch with both
 // policies on 128 shapes (T = 1-8, 256-32768 units, q/k heads shared by 1 or 2 value
 // heads; H = 16), the two alternating over distinct buffer sets so that neither reads what
-// the other left in the last-level cache, and a refreshed H = HV sweep of every launch
-// combination. The device-scope streaming stores win by 1-8 points of HBM peak from 8192
-// units at T >= 2, from 4096 units at T >= 4, at T = 1 from 1024 units (below 8192 with
-// shared q/k heads), at T = 2 on 1024-2047 units, and at T >= 6 on grids of 512-4095 units
-// (512-1023 with shared heads); elsewhere the two are within noise or the plain streaming
-// stores win.
+// the other left in the last-level cache, and refreshed sweeps of every launch combination
+// (HV = H and HV = 2H). The device-scope streaming stores win by 1-8 points of HBM peak
+// from 8192 units at T >= 2, from 4096 units at T >= 4, at T = 1 from 1024 units, at T = 2
+// on 1024-2047 units, and at T >= 6 on grids of 512-4095 units (with shared q/k heads
+// except 1024-2047, where the two-group launch is mixed); elsewhere the two are within
+// noise or the plain streaming stores win.
 int auto_store_128(long long units, int T, int g) {
-  if (T == 1) return units >= 1024 && (g == 1 || units < 8192) ? kStoreNTDev : kStoreNT;
+  if (T == 1) return units >= 1024 ? kStoreNTDev : kStoreNT;
   if (units >= 8192) return kStoreNTDev;
   if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
   if (T == 2 && units >= 1024 && units < 2048) return kStoreNTDev;
-  if (T >= 6 && units >= 512 && (g == 1 || units < 1024)) return kStoreNTDev;
+  if (T >= 6 && units >= 512 && (g == 1 || units < 1024 || units >= 2048)) return kStoreNTDev;
   return kStoreNT;
 }
 

@@ -126,7 +126,9 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
     rows = [json.loads(ln) for ln in open(jsonl) if ln.strip()]
     pct = lambda r, k: 100.0 * r["bytes"] / r["ms"][k] / 1e6 / 8000.0 if k in r["ms"] else float("nan")
     refs = ("32/1", "128/1", "128/1/1", "128/1/1 q")
-    lines = ["# H = HV x T x N sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
+    g = rows[0].get("HV", rows[0]["H"]) // rows[0]["H"]
+    title = "H = HV" if g == 1 else f"H, HV = {g} H"
+    lines = [f"# {title} x T x N sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
              f"Command: `{cmd}` (one MI355X; each shape's buffers rotated so that >= 1 GiB is touched "
              "between reuses; median of >= 8 calls per combination), summarised by "
              f"`python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md {os.path.basename(jsonl)} ...`.",
@@ -138,15 +140,16 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
              "otherwise one workgroup per unit). Percent of the 8 TB/s HBM "
              "peak = algorithmic bytes / kernel time. Shapes of <= 128 units are launch-latency-bound: "
              "their timings include the launch, and the columns differ by noise.", "",
-             "| H=HV | T | N | units | best | best % | AUTO | AUTO % | AUTO/best | " + " | ".join(refs) + " |",
-             "|---|---|---|---|---|---|---|---|---|" + "---|" * len(refs)]
+             "| H | HV | T | N | units | best | best % | AUTO | AUTO % | AUTO/best | " + " | ".join(refs) + " |",
+             "|---|---|---|---|---|---|---|---|---|---|" + "---|" * len(refs)]
     for r in rows:
-        p = kda.make_params(r["N"], r["T"], r["H"], r["H"], 128, 128)
+        p = kda.make_params(r["N"], r["T"], r["H"], r.get("HV", r["H"]), 128, 128)
         ln = kda.select_launch(p)
         auto = (f"{ln['tile_columns']}/{ln['store_policy']}" + (f"/{ln['max_wg_per_cu']}" if ln["max_wg_per_cu"] else "")
                 + (f" g{ln['column_groups']}" if ln["column_groups"] > 1 else "")
                 + (" q" if ln.get("schedule") == 2 else ""))
-        lines.append(f"| {r['H']} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | {r['best_pct']:.1f} | {auto} | "
+        lines.append(f"| {r['H']} | {r.get('HV', r['H'])} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | "
+                     f"{r['best_pct']:.1f} | {auto} | "
                      f"{pct(r, 'auto'):.1f} | {r['auto_over_best']:.3f} | "
                      + " | ".join(f"{pct(r, k):.1f}" if k in r["ms"] else "-" for k in refs) + " |")
     mean = statistics.mean(r["auto_over_best"] for r in rows)

@@ -289,7 +289,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(64, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(64, 8, 16, 32, 128, 128) == (128, 1, 1, 1, 1)
+    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(128, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(256, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(256, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
@@ -298,8 +298,10 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(31, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 1: from 1024 units ...
     assert L(32, 1, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
     assert L(511, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
-    assert L(255, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)      # ... with shared q/k heads below 8192
-    assert L(256, 1, 16, 32, 128, 128) == (128, 1, 2, 1, 1)
+    assert L(31, 1, 16, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... also with shared q/k heads
+    assert L(256, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)
+    assert L(63, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # T >= 6, shared heads: not 1024-2047 units
+    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(31, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 2: 1024-2047 units
     assert L(32, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
     assert L(63, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
