@@ -139,7 +139,7 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
     }
 
 
-def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1) -> None:
+def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts=None) -> None:
     """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
     cap on the grid schedule, and the queue schedule of whole-V workgroups at one per CU in
     1, 2 or 4 column groups (K = V = 128, bf16, softplus). Buffer sets are rotated so that
@@ -155,7 +155,7 @@ def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1) ->
 
     dev = torch.device("cuda:0")
     Hs = tuple(hs) if hs else (8, 32) if quick else (8, 16, 32, 64)
-    Ts = (2, 4, 8) if quick else (1, 2, 4, 6, 8)
+    Ts = tuple(ts) if ts else (2, 4, 8) if quick else (1, 2, 4, 6, 8)
     Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
     combos = [(t, pol, occ, 1, 1) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
     combos += [(128, pol, 1, g, 2) for pol in (1, 2) for g in (1, 2, 4)]
@@ -317,6 +317,7 @@ def main():
                     help="time AUTO's launch with store policy 1 and 2 over T x units x shared heads")
     ap.add_argument("--sweep-h", default="", help="comma-separated H values for --sweep (default all)")
     ap.add_argument("--sweep-g", type=int, default=1, help="value heads per q/k head for --sweep (HV = g H)")
+    ap.add_argument("--sweep-t", default="", help="comma-separated T values for --sweep (default 1,2,4,6,8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -335,7 +336,8 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.sweep:
-        sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x], args.sweep_g)
+        sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x], args.sweep_g,
+              [int(x) for x in args.sweep_t.split(",") if x])
         return
     if args.sweep_store:
         sweep_store(args.sweep_store)

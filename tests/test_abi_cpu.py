@@ -252,7 +252,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     L = lambda *shape, **kw: tuple(kda.select_launch(kda.make_params(*shape, **kw)).values())
     assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0, 1, 1)            # tiny: the only K = V = 16 tile
     assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0, 1, 1)       # small batch: 512 units, T = 4
-    assert L(64, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # GVA: 2048 units, T = 3
+    assert L(64, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)       # GVA: 2048 units, T = 3
     assert L(256, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)      # large batch: 8192 units
     assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 2)      # max bandwidth: 32768 units, T = 8
     assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)           # <= 64 units: latency-bound split
@@ -281,7 +281,9 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T = 3: the grid below 8192 ...
     assert L(256, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(128, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 2)      # ... unless q/k heads are shared
+    assert L(128, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # ... unless q/k heads are shared:
+    assert L(63, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # then the queue from 2048 units
+    assert L(64, 3, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
     assert L(512, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 4, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # shared q/k heads
     assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
