@@ -954,9 +954,9 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 // workgroup launch sits between two units of a CU. Below that the queue's first round is
 // most of the work and its counter traffic does not pay.
 //   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
-//     groups; T >= 2 from 4096 units (T = 3 without shared heads from 8192; from 2048
-//     units T = 2 without shared heads and T = 3 with them: refreshed sweeps, +1.4-5.6 %
-//     and +1.4-3.0 %): two column groups at T = 2, else one;
+//     groups; T >= 2 from 4096 units, and from 2048 at T = 3 and at T = 2 without shared
+//     heads (sweeps with the device-scope streaming stores: +2-7 % at T = 3, +1.4-5.6 %
+//     at T = 2): two column groups at T = 2, else one;
 //   otherwise the grid. Below 1024 units (a sweep of 100 shapes of 128-768 units, T = 1-8,
 //     three timings each), where one generation of workgroups is most of the call and
 //     shorter per-unit chains pay:
@@ -973,8 +973,7 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 Tile auto_shape_128(long long units, int T, int g) {
   // queue schedule, one whole-V workgroup per CU
   if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
-  if ((T >= 2 && units >= 4096 && !(T == 3 && g == 1 && units < 8192)) || (T == 2 && g == 1 && units >= 2048) ||
-      (T == 3 && g > 1 && units >= 2048)) {
+  if ((T >= 2 && units >= 4096) || (T == 2 && g == 1 && units >= 2048) || (T == 3 && units >= 2048)) {
     if (T == 2) return Tile{128, kStoreNT, 1, 2, true};
     return Tile{128, kStoreNT, 1, 1, true};
   }
@@ -1002,7 +1001,7 @@ Tile auto_shape_128(long long units, int T, int g) {
 // noise or the plain streaming stores win.
 int auto_store_128(long long units, int T, int g) {
   if (T == 1) return units >= 1024 ? kStoreNTDev : kStoreNT;
-  if (T == 3 && g > 1 && units >= 2048) return kStoreNTDev;  // with the queue (auto_shape_128)
+  if (T == 3 && units >= 2048) return kStoreNTDev;  // with the queue (auto_shape_128)
   if (units >= 8192) return kStoreNTDev;
   if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
   if (T == 2 && units >= 1024 && units < 2048) return kStoreNTDev;

@@ -279,10 +279,12 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(128, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(128, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T = 3: the grid below 8192 ...
+    assert L(63, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)       # T = 3: the grid below 2048 units ...
+    assert L(64, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)       # ... then the queue, device-scope stores
+    assert L(128, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(256, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(128, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # ... unless q/k heads are shared:
-    assert L(63, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # then the queue from 2048 units
+    assert L(128, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # ... with shared q/k heads too
+    assert L(63, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(64, 3, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
     assert L(512, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 4, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # shared q/k heads
