@@ -139,14 +139,16 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
     }
 
 
-def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts=None) -> None:
+def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts=None, units=None) -> None:
     """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
-    cap on the grid schedule, and the queue schedule of whole-V workgroups at one per CU in
-    1, 2 or 4 column groups (K = V = 128, bf16, softplus). Buffer sets are rotated so that
+    cap on the grid schedule, whole-V workgroups in 2 or 4 column groups on the uncapped grid,
+    and the queue schedule of whole-V workgroups at one per CU in 1, 2 or 4 column groups
+    (K = V = 128, bf16, softplus). Buffer sets are rotated so that
     at least 1 GiB is touched between reuses (small shapes would otherwise run from the
     256 MB last-level cache). A cap is timed only where the grid has more workgroups than
     the cap lets run at once, the queue only where there are more units than CUs.
-    heads_per_qk > 1 gives each q/k head that many value heads (HV = heads_per_qk H). Writes one JSON object per shape to
+    heads_per_qk > 1 gives each q/k head that many value heads (HV = heads_per_qk H); units =
+    (lo, hi) keeps only the shapes with lo <= N HV <= hi. Writes one JSON object per shape to
     out_path and prints a summary line."""
     import torch
 
@@ -158,6 +160,7 @@ def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts
     Ts = tuple(ts) if ts else (2, 4, 8) if quick else (1, 2, 4, 6, 8)
     Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
     combos = [(t, pol, occ, 1, 1) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
+    combos += [(128, pol, 8, g, 1) for pol in (1, 2) for g in (2, 4)]
     combos += [(128, pol, 1, g, 2) for pol in (1, 2) for g in (1, 2, 4)]
     rows = []
     with open(out_path, "w") as f:
@@ -165,6 +168,8 @@ def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts
             for T in Ts:
                 for N in Ns:
                     HV = heads_per_qk * H
+                    if units and not units[0] <= N * HV <= units[1]:
+                        continue
                     w = synth.Workload(f"sweep", N=N, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16",
                                        gate="softplus", seed=1)
                     b_alg = synth.algorithmic_bytes(w)
@@ -318,6 +323,8 @@ def main():
     ap.add_argument("--sweep-h", default="", help="comma-separated H values for --sweep (default all)")
     ap.add_argument("--sweep-g", type=int, default=1, help="value heads per q/k head for --sweep (HV = g H)")
     ap.add_argument("--sweep-t", default="", help="comma-separated T values for --sweep (default 1,2,4,6,8)")
+    ap.add_argument("--sweep-units", default="", metavar="LO,HI",
+                    help="keep only the --sweep shapes with LO <= N HV <= HI units")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -337,7 +344,8 @@ def main():
 
     if args.sweep:
         sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x], args.sweep_g,
-              [int(x) for x in args.sweep_t.split(",") if x])
+              [int(x) for x in args.sweep_t.split(",") if x],
+              tuple(int(x) for x in args.sweep_units.split(",")) if args.sweep_units else None)
         return
     if args.sweep_store:
         sweep_store(args.sweep_store)

@@ -962,7 +962,8 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 //     shorter per-unit chains pay:
 //     <= 64 units, and <= 128 at T = 2: the 32-column split (4 WGs per unit);
 //     <= 128 units: whole V in four column groups; 129-447: whole V in two column groups
-//     (T = 1: four below 320 units, else one); 448-512: whole V;
+//     (T = 1: four below 320 units, else one; T = 3, 5, 7 from 256 units: one group, with
+//     the device-scope stores); 448-512: whole V;
 //     513-1023: whole V at T <= 2, else one WG per CU in two groups;
 //   from 1024 units, whole V: T <= 2: two WGs per CU (64 columns at T = 2 from 2048);
 //     T <= 5: one WG per CU in two column groups; T >= 6: one WG per CU, with shared q/k
@@ -980,7 +981,10 @@ Tile auto_shape_128(long long units, int T, int g) {
   // the grid: below 1024 units
   if (units <= 64 || (units <= 128 && T == 2)) return Tile{32, kStoreNT};
   if (units <= 128) return Tile{128, kStoreNT, 0, 4};
-  if (units < 448) return Tile{128, kStoreNT, 0, T > 1 ? 2 : units < 320 ? 4 : 1};
+  if (units < 448) {
+    if (units >= 256 && (T == 3 || T == 5 || T == 7)) return Tile{128, kStoreNT};  // see auto_store_128
+    return Tile{128, kStoreNT, 0, T > 1 ? 2 : units < 320 ? 4 : 1};
+  }
   if (units <= 512) return Tile{128, kStoreNT};
   if (units < 1024) return T <= 2 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 1, 2};
   // the grid from 1024 units
@@ -997,10 +1001,14 @@ Tile auto_shape_128(long long units, int T, int g) {
 // (HV = H and HV = 2H). The device-scope streaming stores win by 1-8 points of HBM peak
 // from 8192 units at T >= 2, from 4096 units at T >= 4, at T = 1 from 1024 units, at T = 2
 // on 1024-2047 units, and at T >= 6 on grids of 512-4095 units (with shared q/k heads
-// except 1024-2047, where the two-group launch is mixed); elsewhere the two are within
-// noise or the plain streaming stores win.
+// except 1024-2047, where the two-group launch is mixed). On grids of 256-447 units at
+// T = 3, 5 and 7, one whole-V group with the device-scope stores beat two groups with the
+// plain streaming stores in repeated sweeps at 256 units (+1-4 % at T = 3, 0-4 % at T = 5,
+// +2-8 % at T = 7, H = HV and HV = 2H), while the same launch lost 3-8 % at T = 4 and 8 and
+// was mixed at T = 6. Elsewhere the two are within noise or the plain streaming stores win.
 int auto_store_128(long long units, int T, int g) {
   if (T == 1) return units >= 1024 ? kStoreNTDev : kStoreNT;
+  if (units >= 256 && units < 448 && (T == 3 || T == 5 || T == 7)) return kStoreNTDev;
   if (T == 3 && units >= 2048) return kStoreNTDev;  // with the queue (auto_shape_128)
   if (units >= 8192) return kStoreNTDev;
   if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;

@@ -3,7 +3,7 @@
   python -m linear_attention_decode_kda_amd.rocprof_summary stats <kernel_stats.csv> <cmd> <out.md>
   python -m linear_attention_decode_kda_amd.rocprof_summary traffic <workload> <variant>
          <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <cmd-file> <out.json>
-  python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md <sweep.jsonl> <cmd> <out.md>
+  python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md <sweep.jsonl> <cmd> <out.md> [refs]
   python -m linear_attention_decode_kda_amd.rocprof_summary store-md <sweep_store.jsonl> <cmd> <out.md>
 
 `traffic` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the verify
@@ -118,14 +118,15 @@ def traffic(workload, variant, fetch, write, cfetch, cwrite, cmd_file, out) -> N
         f.write("\n")
 
 
-def sweep_md(jsonl: str, cmd: str, out: str) -> None:
+def sweep_md(jsonl: str, cmd: str, out: str, refs: str = "") -> None:
     """Table of a `bench.py --sweep` run: per shape the best (tile/store[/cap]) and its
-    share of the HBM peak, the AUTO choice and its share, and three reference launches."""
+    share of the HBM peak, the AUTO choice and its share, and reference launches (refs,
+    comma-separated combination labels; four by default)."""
     import linear_attention_decode_kda_amd as kda
 
     rows = [json.loads(ln) for ln in open(jsonl) if ln.strip()]
     pct = lambda r, k: 100.0 * r["bytes"] / r["ms"][k] / 1e6 / 8000.0 if k in r["ms"] else float("nan")
-    refs = ("32/1", "128/1", "128/1/1", "128/1/1 q")
+    refs = tuple(refs.split(",")) if refs else ("32/1", "128/1", "128/1/1", "128/1/1 q")
     g = rows[0].get("HV", rows[0]["H"]) // rows[0]["H"]
     title = "H = HV" if g == 1 else f"H, HV = {g} H"
     lines = [f"# {title} x T x N sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
@@ -166,7 +167,7 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10])
     elif sys.argv[1] == "sweep-md":
-        sweep_md(*sys.argv[2:5])
+        sweep_md(*sys.argv[2:6])
     elif sys.argv[1] == "store-md":
         store_md(*sys.argv[2:5])
     else:

@@ -262,6 +262,11 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 4, 1)        # 129-447 units: four groups at T = 1 ...
     assert L(12, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... (one from 320)
     assert L(12, 4, 32, 32, 128, 128) == (128, 1, 0, 2, 1)       # ... else two
+    assert L(8, 3, 32, 32, 128, 128) == (128, 2, 0, 1, 1)        # ... but at T = 3, 5, 7 from 256 units one,
+    assert L(13, 7, 32, 32, 128, 128) == (128, 2, 0, 1, 1)       #     with device-scope stores
+    assert L(8, 5, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(7, 3, 16, 32, 128, 128) == (128, 1, 0, 2, 1)        #     (224 units: two groups)
+    assert L(14, 5, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       #     (448 units: the next bucket)
     assert L(16, 8, 16, 16, 128, 128) == (128, 1, 0, 2, 1)
     assert L(24, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # 513-1023 units
     assert L(24, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)
