@@ -141,8 +141,8 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
 
 def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts=None, units=None) -> None:
     """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
-    cap on the grid schedule, whole-V workgroups in 2 or 4 column groups on the uncapped grid,
-    and the queue schedule of whole-V workgroups at one per CU in 1, 2 or 4 column groups
+    cap on the grid schedule, whole-V workgroups in 2 or 4 column groups on the uncapped grid
+    and in 2 at one per CU, and the queue schedule of whole-V workgroups at one per CU in 1, 2 or 4 column groups
     (K = V = 128, bf16, softplus). Buffer sets are rotated so that
     at least 1 GiB is touched between reuses (small shapes would otherwise run from the
     256 MB last-level cache). A cap is timed only where the grid has more workgroups than
@@ -161,6 +161,7 @@ def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts
     Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
     combos = [(t, pol, occ, 1, 1) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
     combos += [(128, pol, 8, g, 1) for pol in (1, 2) for g in (2, 4)]
+    combos += [(128, pol, 1, 2, 1) for pol in (1, 2)]
     combos += [(128, pol, 1, g, 2) for pol in (1, 2) for g in (1, 2, 4)]
     rows = []
     with open(out_path, "w") as f:
