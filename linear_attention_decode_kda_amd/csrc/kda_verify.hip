@@ -962,8 +962,8 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 //     shorter per-unit chains pay:
 //     <= 64 units, and <= 128 at T = 2: the 32-column split (4 WGs per unit);
 //     <= 128 units: whole V in four column groups; 129-447: whole V in two column groups
-//     (T = 1: four below 320 units, else one; T = 3, 5, 7 from 256 units: one group, with
-//     the device-scope stores); 448-512: whole V;
+//     (T = 1: four below 320 units, else one; T = 3, 5, 7 from 256 units: one group; the
+//     store policy there in auto_store_128); 448-512: whole V;
 //     513-1023: whole V at T <= 2, else one WG per CU in two groups;
 //   from 1024 units, whole V: T <= 2: two WGs per CU (64 columns at T = 2 from 2048);
 //     T <= 5: one WG per CU in two column groups; T >= 6: one WG per CU, with shared q/k
@@ -1002,13 +1002,19 @@ Tile auto_shape_128(long long units, int T, int g) {
 // from 8192 units at T >= 2, from 4096 units at T >= 4, at T = 1 from 1024 units, at T = 2
 // on 1024-2047 units, and at T >= 6 on grids of 512-4095 units (with shared q/k heads
 // except 1024-2047, where the two-group launch is mixed). On grids of 256-447 units at
-// T = 3, 5 and 7, one whole-V group with the device-scope stores beat two groups with the
-// plain streaming stores in repeated sweeps at 256 units (+1-4 % at T = 3, 0-4 % at T = 5,
-// +2-8 % at T = 7, H = HV and HV = 2H), while the same launch lost 3-8 % at T = 4 and 8 and
-// was mixed at T = 6. Elsewhere the two are within noise or the plain streaming stores win.
-int auto_store_128(long long units, int T, int g) {
+// T = 3-8 (repeated sweeps at 256 units with HV = 8-64 and at 384 units with HV = 12-48):
+// at T = 3, 5 and 7, one whole-V group with the device-scope stores beat two groups with
+// the plain streaming stores (+1-4 % at T = 3, 0-4 % at T = 5, +2-8 % at T = 7); at even T
+// the two-group launch gains from the device-scope stores (+1.4 % at T = 6 with HV a power
+// of two; +1.4-5.2 % at T = 4, 6, 8 with HV = 12, 24, 48) except where a sequence's
+// snapshots span a power of two (T HV 64 KiB; T = 4, 8 with HV a power of two: -0.3 to
+// -0.9 %). Elsewhere the two policies are within noise or the plain streaming stores win.
+int auto_store_128(long long units, int T, int g, int HV) {
   if (T == 1) return units >= 1024 ? kStoreNTDev : kStoreNT;
-  if (units >= 256 && units < 448 && (T == 3 || T == 5 || T == 7)) return kStoreNTDev;
+  if (units >= 256 && units < 448 && T >= 3 && T <= 8) {
+    const long long span = (long long)T * HV;  // snapshot rows of one sequence, in units of 64 KiB
+    if (T % 2 == 1 || (span & (span - 1)) != 0) return kStoreNTDev;
+  }
   if (T == 3 && units >= 2048) return kStoreNTDev;  // with the queue (auto_shape_128)
   if (units >= 8192) return kStoreNTDev;
   if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
@@ -1017,9 +1023,9 @@ int auto_store_128(long long units, int T, int g) {
   return kStoreNT;
 }
 
-Tile auto_tile_128(long long units, int T, int g) {
+Tile auto_tile_128(long long units, int T, int g, int HV) {
   Tile t = auto_shape_128(units, T, g);
-  t.stp = auto_store_128(units, T, g);
+  t.stp = auto_store_128(units, T, g, HV);
   return t;
 }
 
@@ -1031,7 +1037,7 @@ Tile choose_tile(const kda_verify_params* p) {
   const bool caller_tile = p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO;
   Tile t;
   if (K == 128 && V == 128) {
-    t = auto_tile_128((long long)p->N * p->HV, p->T, p->HV / p->H);
+    t = auto_tile_128((long long)p->N * p->HV, p->T, p->HV / p->H, p->HV);
     if (caller_tile) {
       t.occ = 0;
       t.g = 1;

@@ -267,6 +267,12 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(8, 5, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(7, 3, 16, 32, 128, 128) == (128, 1, 0, 2, 1)        #     (224 units: two groups)
     assert L(14, 5, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       #     (448 units: the next bucket)
+    # ... even T: device-scope stores unless a sequence's snapshots span a power of two
+    # (T HV = 128 for the two "else two" shapes above; 48, 192 and 96 here)
+    assert L(32, 4, 12, 12, 128, 128) == (128, 2, 0, 2, 1)
+    assert L(16, 8, 8, 24, 128, 128) == (128, 2, 0, 2, 1)
+    assert L(8, 6, 16, 32, 128, 128) == (128, 2, 0, 2, 1)
+    assert L(8, 9, 32, 32, 128, 128) == (128, 1, 0, 2, 1)        #     (measured up to T = 8 only)
     assert L(16, 8, 16, 16, 128, 128) == (128, 1, 0, 2, 1)
     assert L(24, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # 513-1023 units
     assert L(24, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)
@@ -294,7 +300,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(512, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 4, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # shared q/k heads
     assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(8, 6, 32, 32, 128, 128) == (128, 1, 0, 2, 1)        # T >= 6
+    assert L(8, 6, 32, 32, 128, 128) == (128, 2, 0, 2, 1)        # T >= 6 (256-447 units: see the span rule)
     assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(64, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
