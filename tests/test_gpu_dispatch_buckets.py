@@ -1,0 +1,63 @@
+"""Every branch of the dispatch rule on grids of 256-447 (sequence, value head) units, on
+the GPU through the C ABI: one whole-V group with the device-scope streaming stores at odd
+T; two groups at even T, with the device-scope stores unless a sequence's snapshots span a
+power of two (T HV blocks of K V floats); value-head counts that are not powers of two
+among them (HV = 12, 24, 48).
+
+For each shape the launch AUTO picks is pinned, its results must equal those of the
+32-column split bit for bit (every launch shares the K split and the partial-sum tree),
+conv_window and the rolled conv_state must equal the shift-register definition bit for bit,
+and o and inter_ssm of sampled sequences must be within max-abs 2e-3 of the float64 oracle.
+
+Page: "[KDA] Fuse causal conv1d into MTP verify decode #107" (cuLA pull request), PR
+description (small and large variants share one API and math; HV >= H) and Tests &
+Accuracy (variants bit-identical, conv state bit-exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_decode_kda_amd as kda
+import oracle
+from linear_attention_decode_kda_amd import synth
+from gpu_util import assert_matches, bits, ref_bits, run_gpu, say, slice_inputs
+
+pytestmark = pytest.mark.gpu
+
+# (N, T, H, HV, gate) -> the launch AUTO must pick: (tile, store policy, cap, groups, schedule)
+CASES = [
+    ((16, 7, 16, 16, "softplus"), (128, 2, 0, 1, 1)),   # 256 units, odd T: one group
+    ((32, 3, 12, 12, "safe"), (128, 2, 0, 1, 1)),       # 384 units, odd T, HV = 12
+    ((8, 4, 32, 32, "safe"), (128, 1, 0, 2, 1)),        # 256 units, T HV = 128: streaming stores
+    ((16, 4, 8, 24, "softplus"), (128, 2, 0, 2, 1)),    # 384 units, T HV = 96
+    ((16, 6, 8, 24, "safe"), (128, 2, 0, 2, 1)),        # 384 units, T HV = 144
+    ((8, 8, 16, 48, "softplus"), (128, 2, 0, 2, 1)),    # 384 units, T HV = 384
+]
+
+
+def _bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+    dt = torch.int16 if a.element_size() == 2 else torch.int32
+    return torch.equal(a.view(dt), b.view(dt))
+
+
+@pytest.mark.parametrize("shape,launch", CASES, ids=[f"N{c[0][0]}-T{c[0][1]}-H{c[0][2]}-HV{c[0][3]}" for c in CASES])
+def test_bucket_launch_and_parity(shape, launch):
+    N, T, H, HV, gate = shape
+    w = synth.Workload(f"bucket-N{N}-T{T}-H{H}-HV{HV}", N=N, T=T, H=H, HV=HV, K=128, V=128,
+                       dtype="bf16", gate=gate, seed=7000 + 10 * T + HV)
+    assert tuple(kda.select_launch(kda.params_for(w)).values()) == launch
+    inp = synth.make_inputs(w)
+    x0, cs0 = inp["mixed_qkv"].clone(), inp["conv_state"].clone()
+    auto = run_gpu(w, inp, kda.VARIANT_AUTO)
+    split = run_gpu(w, inp, kda.VARIANT_SMALL)
+    for k in ("o", "inter_ssm", "conv_window", "conv_state"):
+        assert _bits_equal(auto[k], split[k]), f"{w.name}: {k} differs between AUTO {launch} and the 32-column split"
+    del split
+    cw_ref, cs_ref = oracle.conv_roll(x0, cs0)
+    assert np.array_equal(bits(auto["conv_window"]), ref_bits(cw_ref, w.torch_dtype)), f"{w.name}: conv_window"
+    assert np.array_equal(bits(auto["conv_state"]), ref_bits(cs_ref, w.torch_dtype)), f"{w.name}: conv_state"
+    sample = np.unique(np.array([0, N // 2, N - 1]))
+    ref = oracle.verify_workload(w.with_(N=len(sample)), slice_inputs(inp, sample))
+    err = assert_matches(w, auto, ref, n_index=sample, what=f"{w.name} sampled n={sample.tolist()}")
+    say(f"{w.name}: launch {launch}, bit-identical to the split, sampled max-abs o={err['o']:.2e} "
+        f"inter_ssm={err['inter_ssm']:.2e}")
