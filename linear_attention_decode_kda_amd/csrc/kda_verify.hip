@@ -954,9 +954,12 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 // workgroup launch sits between two units of a CU. Below that the queue's first round is
 // most of the work and its counter traffic does not pay.
 //   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
-//     groups; T >= 2 from 4096 units, and from 2048 at T = 3 and at T = 2 without shared
-//     heads (sweeps with the device-scope streaming stores: +2-7 % at T = 3, +1.4-5.6 %
-//     at T = 2): two column groups at T = 2, else one;
+//     groups; T = 2 from 4096 units, and from 2048 without shared heads (+1.4-5.6 %), in
+//     two column groups; T = 3-5 from 2048 units and T >= 6 from 2560, in one (with the
+//     device-scope streaming stores: +2-7 % at T = 3; at T = 4-8, timed against the grid
+//     on 2048 and 3072 units with 16-256 sequences, +2-10 % at 3072, +1.6 and +2.1 % on
+//     average at T = 4 and 5 on 2048, where T = 6-8 gain nothing and lose up to 3 % at
+//     T = 8 with many sequences);
 //   otherwise the grid. Below 1024 units (a sweep of 100 shapes of 128-768 units, T = 1-8,
 //     three timings each), where one generation of workgroups is most of the call and
 //     shorter per-unit chains pay:
@@ -974,7 +977,8 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 Tile auto_shape_128(long long units, int T, int g) {
   // queue schedule, one whole-V workgroup per CU
   if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
-  if ((T >= 2 && units >= 4096) || (T == 2 && g == 1 && units >= 2048) || (T == 3 && units >= 2048)) {
+  if ((T >= 2 && units >= 4096) || (T == 2 && g == 1 && units >= 2048) || (T >= 3 && T <= 5 && units >= 2048) ||
+      (T >= 6 && units >= 2560)) {
     if (T == 2) return Tile{128, kStoreNT, 1, 2, true};
     return Tile{128, kStoreNT, 1, 1, true};
   }
@@ -999,9 +1003,10 @@ Tile auto_shape_128(long long units, int T, int g) {
 // heads; H = 16), the two alternating over distinct buffer sets so that neither reads what
 // the other left in the last-level cache, and refreshed sweeps of every launch combination
 // (HV = H and HV = 2H). The device-scope streaming stores win by 1-8 points of HBM peak
-// from 8192 units at T >= 2, from 4096 units at T >= 4, at T = 1 from 1024 units, at T = 2
-// on 1024-2047 units, and at T >= 6 on grids of 512-4095 units (with shared q/k heads
-// except 1024-2047, where the two-group launch is mixed). On grids of 256-447 units at
+// from 8192 units at T >= 2, on the queue from 2048 units at T >= 3 (2-4 % over the plain
+// streaming stores on that queue), at T = 1 from 1024 units, at T = 2 on 1024-2047 units,
+// and at T >= 6 on grids of 512-2047 units (with shared q/k heads below 1024, where the
+// two-group launch is otherwise mixed). On grids of 256-447 units at
 // T = 3-8 (repeated sweeps at 256 units with HV = 8-64 and at 384 units with HV = 12-48):
 // at T = 3, 5 and 7, one whole-V group with the device-scope stores beat two groups with
 // the plain streaming stores (+1-4 % at T = 3, 0-4 % at T = 5, +2-8 % at T = 7); at even T
@@ -1015,7 +1020,7 @@ int auto_store_128(long long units, int T, int g, int HV) {
     const long long span = (long long)T * HV;  // snapshot rows of one sequence, in units of 64 KiB
     if (T % 2 == 1 || (span & (span - 1)) != 0) return kStoreNTDev;
   }
-  if (T == 3 && units >= 2048) return kStoreNTDev;  // with the queue (auto_shape_128)
+  if (T >= 3 && units >= 2048) return kStoreNTDev;  // the queue, or the capped grid at T >= 6
   if (units >= 8192) return kStoreNTDev;
   if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
   if (T == 2 && units >= 1024 && units < 2048) return kStoreNTDev;

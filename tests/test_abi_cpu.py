@@ -287,7 +287,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(512, 2, 64, 64, 128, 128) == (128, 2, 1, 2, 2)
     assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T <= 5
     assert L(32, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(127, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(63, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)       # T = 3: the grid below 2048 units ...
@@ -303,6 +303,8 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(8, 6, 32, 32, 128, 128) == (128, 2, 0, 2, 1)        # T >= 6 (256-447 units: see the span rule)
     assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(64, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
+    assert L(79, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)       # T >= 6: the queue from 2560 units
+    assert L(80, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(128, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
@@ -316,7 +318,6 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(31, 1, 16, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... also with shared q/k heads
     assert L(256, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)
     assert L(63, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # T >= 6, shared heads: not 1024-2047 units
-    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
     assert L(31, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 2: 1024-2047 units
     assert L(32, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
     assert L(63, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
@@ -324,25 +325,28 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(64, 2, 16, 32, 128, 128) == (64, 1, 2, 1, 1)        # ... the grid with shared q/k heads
     assert L(255, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2: from 8192 units
     assert L(256, 2, 32, 32, 128, 128) == (128, 2, 1, 2, 2)
-    assert L(127, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)      # T >= 4: from 4096 units
-    assert L(128, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(63, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)       # T = 3-5: from 2048 units (the queue)
+    assert L(64, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(64, 5, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(96, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)        # 3072 units
     assert L(15, 6, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T >= 6: from 512 units ...
     assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
-    assert L(127, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
+    assert L(63, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
+    assert L(127, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
     assert L(16, 6, 16, 32, 128, 128) == (128, 2, 0, 1, 1)       # ... with shared q/k heads below 1024
     assert L(32, 6, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6, 1, 1)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 2, 0, 1, 1)   # the AUTO cap goes with its tile
-    assert L(64, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: no AUTO cap
-    assert L(64, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0, 2, 1)   # 8: explicitly none
-    assert L(64, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2, 1, 1)
-    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 1, 0, 1, 1)
-    assert L(64, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 1, 0, 1, 1)
-    assert L(64, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1, 2, 1)
-    assert L(64, 4, 32, 32, 128, 128, column_groups=4) == (128, 1, 1, 4, 1)
+    assert L(32, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: no AUTO cap
+    assert L(32, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0, 2, 1)   # 8: explicitly none
+    assert L(32, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 1, 0, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 1, 0, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1, 2, 1)
+    assert L(32, 4, 32, 32, 128, 128, column_groups=4) == (128, 1, 1, 4, 1)
     assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2, 1, 1)
     assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 2, 1, 1, 1)      # the grid, AUTO cap kept
-    assert L(64, 4, 32, 32, 128, 128, schedule=2) == (128, 1, 1, 2, 2)
+    assert L(32, 4, 32, 32, 128, 128, schedule=2) == (128, 1, 1, 2, 2)
     assert L(1, 4, 8, 8, 128, 128, schedule=2) == (128, 1, 0, 1, 2)          # the queue takes whole V
     assert L(8, 4, 16, 16, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: one group
     assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 2, 0, 1, 2)

@@ -231,8 +231,8 @@ def test_zero_q_k_channels():
     assert torch.count_nonzero(got["o"]) == 0
 
 
-@pytest.mark.parametrize("w", [W(64, 4, 16, 32, 128, 128, gate="safe"),   # 2048 units at T = 4, streaming stores
-                               W(16, 4, 8, 16, 128, 128),                  # 256 units, device-scope streaming stores
+@pytest.mark.parametrize("w", [W(64, 4, 16, 32, 128, 128, gate="safe"),   # 2048 units at T = 4, device-scope streaming stores
+                               W(16, 4, 8, 16, 128, 128),                  # 256 units, T HV = 64: streaming stores
                                W(32, 8, 16, 32, 128, 128, gate="safe")])   # T = 8, shared q/k heads, 1024 units: streaming
 def test_every_tile_shape_bit_identical(w):
     """SMALL (32-column WGs) and LARGE (whole-V WGs) with the store policy dispatch picks for
