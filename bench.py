@@ -83,6 +83,29 @@ def host_threads() -> int:
     return max(1, min(16, n))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_description(threads: int) -> dict:
+    """What the CPU baseline ran on: the oracle's worker threads, the host's logical CPUs
+    (os.cpu_count), the CPUs this process may run on (its affinity mask) and the CPU model."""
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return {"threads": threads, "host_cores": os.cpu_count() or 1, "cpus_allowed": allowed,
+            "cpu_model": cpu_model()}
+
+
 def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
     """The oracle as it is (float64, sequential C) on bounded samples of the same inputs,
     run on slices of 4 sequences: (1) on one host thread over the first n sequences, n
@@ -132,6 +155,8 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        **host_description(threads),
+        "role": "a baseline for context, not the target",
         "sample": f"first {n_mt} of {w.N} sequences ({n_mt * w.HV} of {w.units} (sequence, value-head) units), "
                   f"all T={w.T} tokens, same inputs, {passes} pass(es), in slices of {chunk} sequences over "
                   f"{threads} host threads; {el_mt:.1f} s",

@@ -176,9 +176,12 @@ kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_
  * int32 array of N entries, or NULL for the identity (sequence n uses row n, and the
  * pool then has N rows). Sequence n is a padding entry when any of its three indices is
  * negative or not below the pool's row count: nothing is read or written for it (its
- * rows of o are left as they were). Rows written by one call (conv_state and the two
- * intermediate pools) must be distinct across the batch; the state pool is only read
- * by a verify call and may be shared. */
+ * rows of o are left as they were). Rows written by one verify call (conv_state and the
+ * two intermediate pools) must be distinct across the batch; a verify call only reads the
+ * state pool, so sequences may share a state row there (a commit writes it: see
+ * kda_verify_commit). The library does not read the device index arrays on the host, so
+ * it cannot check distinctness: duplicated written rows race, and such a row ends up
+ * holding an unspecified mix of the sequences' values. */
 typedef struct {
   const int32_t* conv_state_indices;         /* row of conv_state [conv_state_slots, C, 3] */
   const int32_t* cache_indices;              /* row of state [state_slots, HV, K, V] */
@@ -223,7 +226,16 @@ kda_status kda_conv_verify_decode_unfused(const kda_verify_params* p, const kda_
  *   state[cache_indices[n]]           <- inter_ssm[intermediate_state_indices[n], a_n - 1]
  *   conv_state[conv_state_indices[n]] <- conv_window[intermediate_state_indices[n], a_n - 1]
  * Bit copies. Sequences with a_n outside [1, T], and padding entries, are left alone.
- * p gives N, T, H, HV, K, V and in_dtype; pools as above (NULL = identity). */
+ * p gives N, T, H, HV, K, V and in_dtype; pools as above (NULL = identity).
+ * The rows a commit writes must be distinct among the sequences it commits (a_n in
+ * [1, T], not padding): two of them with the same cache_indices row, or the same
+ * conv_state_indices row, race, and that row then holds an unspecified mix of their
+ * snapshots. Sequences that are not committed may share rows with anything. The index
+ * arrays are device memory that the host does not read, so this is the caller's
+ * contract and is not checked; NULL index arrays (the identity) are distinct by
+ * construction. Host-side checks: NULL or misaligned pointers (KDA_ERR_NULL,
+ * KDA_ERR_ALIGN), pool sizes (KDA_ERR_SHAPE), written ranges overlapping read ones or
+ * each other (KDA_ERR_ALIAS); a rejected call launches nothing. */
 kda_status kda_verify_commit(const kda_verify_params* p, const kda_pool_desc* pools,
                              const int32_t* accepted, const float* inter_ssm,
                              const void* conv_window, float* state, void* conv_state,

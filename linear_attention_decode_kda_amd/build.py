@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "kda_verify.hip")
 HDR = os.path.join(ROOT, "include", "kda_verify.h")
+QHDR = os.path.join(PKG, "csrc", "kda_queue.h")
 LIB = os.path.join(PKG, "libkda_verify.so")
 ARCH = "gfx950"
 
@@ -49,7 +50,7 @@ def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in (SRC, HDR))
+    return any(os.path.getmtime(p) > t for p in (SRC, HDR, QHDR))
 
 
 if __name__ == "__main__":

@@ -50,6 +50,8 @@
 #include <type_traits>
 
 #include "kda_verify.h"
+#define KDA_HOST_DEVICE __host__ __device__
+#include "kda_queue.h"
 
 namespace kda {
 
@@ -319,7 +321,7 @@ struct alignas(16) Smem {
   alignas(16) float dtb[CF::K];
   R bs[CF::TMAX];
   int last;
-  int next[2];  // queue schedule: the unit after the current one, by iteration parity
+  uint32_t next[2];  // queue schedule: the ticket for the next unit, by iteration parity
 };
 
 template <class CF>
@@ -344,10 +346,11 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
 
   const int tid = threadIdx.x;
-  // The ticket is set in thread 0 only and read back from wave 0's first lane. It is left
-  // uninitialised elsewhere on purpose: any write to its register at the top of a unit
-  // (a zero, or an empty asm that defines it) makes the wave wait first for every store
-  // of the previous unit still in flight.
+  // The ticket is drawn by thread 0 and read only by thread 0, on the same path, so no
+  // other lane ever reads it. It gets no initial value on purpose: one would make the
+  // compiler set the register at the top of every unit, and that write waits first for
+  // every store of the previous unit still in flight (measured; a zero, an empty asm
+  // defining it and __builtin_nondeterministic_value all do).
   uint32_t ticket;
   if constexpr (QUEUE)
     if (tid == 0)
@@ -366,10 +369,8 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
       in_row >= a.in_slots) {
     // padding entry: the whole unit (and its group) skips, nothing is read or written
-    if constexpr (QUEUE) {
-      const int nxt = __builtin_amdgcn_readfirstlane((int)ticket);
-      if (tid == 0) s.next[slot] = nxt;
-    }
+    if constexpr (QUEUE)
+      if (tid == 0) s.next[slot] = ticket;
     return;
   }
 
@@ -443,8 +444,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   if (tid < T) s.bs[tid] = bval;
   if constexpr (QUEUE) {
     // the ticket was issued before the staged loads just waited for, so it has landed
-    const int nxt = __builtin_amdgcn_readfirstlane((int)ticket);
-    if (tid == 0) s.next[slot] = nxt;
+    if (tid == 0) s.next[slot] = ticket;
   }
   __syncthreads();  // B0: staged inputs visible; this WG's conv-cache reads have landed
 
@@ -742,12 +742,12 @@ template <class CF, typename R>
 __global__ __launch_bounds__(CF::NTHR) void kda_verify_queue_kernel(const Args a) {
   __shared__ Smem<CF, R> s;
   const int units = a.N * a.HV * CF::NVT;
-  const int G = gridDim.x;
+  const int G = gridDim.x;  // <= units
   int lb = xcd_order(blockIdx.x, G);
-  for (int it = 0; lb < units; ++it) {
+  for (int it = 0; lb >= 0; ++it) {
     verify_unit<CF, R, true>(a, s, lb, it & 1);
     __syncthreads();  // the unit's LDS reads are done before the next unit stages inputs
-    lb = G + s.next[it & 1];
+    lb = kda_queue_unit(s.next[it & 1], units, G);
   }
   if (threadIdx.x == 0) {
     uint32_t* q = a.counters + (size_t)a.N * a.H;
@@ -1054,8 +1054,8 @@ Tile choose_tile(const kda_verify_params* p) {
       t.vt = 128;
     else if (p->variant == KDA_VARIANT_SMALL)
       t.vt = 32;
-    else if (p->schedule == 2)
-      t.vt = 128;  // the queue runs whole-V workgroups
+    else if (p->schedule == 2 || p->column_groups > 1)
+      t.vt = 128;  // the queue and column groups run whole-V workgroups
     if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreNTDev : kStoreNT;
     // fp32 inputs at T > 8: a whole-V workgroup's staged inputs and conv windows would not
     // fit in LDS; two 64-column workgroups give the same bits

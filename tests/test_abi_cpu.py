@@ -198,6 +198,33 @@ def test_commit_validation(lib):
     assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -7
     p0 = kda.make_params(0, 4, 2, 4, 128, 128)
     assert lib.kda_verify_commit(ctypes.byref(p0), None, *args([0] * 5), None) == 0
+    bad = list(ptrs)
+    bad[0] += 2  # misaligned accepted lengths
+    assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -4
+    bad = list(ptrs)
+    bad[0] = ptrs[3] + 64  # accepted lengths inside the state pool the commit writes
+    assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -7
+    bad = list(ptrs)
+    bad[4] = ptrs[3]  # conv_state and state written over one another
+    assert lib.kda_verify_commit(ctypes.byref(p), None, *args(bad), None) == -7
+    pd = kda.PoolDesc()
+    pd.conv_state_slots, pd.state_slots, pd.intermediate_slots = 4, 3, 4
+    assert lib.kda_verify_commit(ctypes.byref(p), ctypes.byref(pd), *args(ptrs), None) == -2  # identity needs N rows
+    pd.state_slots = 8
+    pd.cache_indices = ptrs[3] + 16  # an index array inside the state pool, which the commit writes
+    assert lib.kda_verify_commit(ctypes.byref(p), ctypes.byref(pd), *args(ptrs), None) == -7
+    bad_p = kda.make_params(4, 4, 2, 4, 128, 128)
+    bad_p.HV = 5
+    assert lib.kda_verify_commit(ctypes.byref(bad_p), None, *args(ptrs), None) == -2
+
+
+def test_commit_contract_is_stated_in_the_header():
+    """Distinct written rows among committed sequences are the caller's contract (the
+    index arrays are device memory the host never reads); the header says so."""
+    src = open(HEADER).read()
+    head = src[src.index("kda_status kda_verify_commit") - 2200:src.index("kda_status kda_verify_commit")]
+    assert "must be distinct among the sequences it commits" in head
+    assert "is not checked" in head and "race" in head
 
 
 def test_tuning_overrides(lib):
@@ -229,6 +256,39 @@ def test_tuning_overrides(lib):
         p = kda.make_params(8, 4, 2, 2, 128, 128, **good)
         ptrs, wsb = _fake_ptrs(p)
         assert _validate(lib, p, ptrs, wsb) == 0, good
+
+
+# launches a kernel exists for at K = V = 128: (columns per workgroup, column groups)
+BUILT_128 = {(128, 1), (128, 2), (128, 4), (64, 1), (32, 1)}
+
+
+def test_every_accepted_override_names_a_built_launch(lib):
+    """Any combination of overrides that validates resolves to a launch some kernel
+    implements: column groups split whole-V workgroups only, so asking for groups without a
+    tile takes whole V even where AUTO's own tile is narrower (T = 2 with shared q/k heads
+    on 2048 units, where AUTO runs 64 columns)."""
+    p = kda.make_params(64, 2, 16, 32, 128, 128)
+    assert kda.select_launch(p)["tile_columns"] == 64
+    p = kda.make_params(64, 2, 16, 32, 128, 128, column_groups=2)
+    assert tuple(kda.select_launch(p).values()) == (128, 1, 2, 2, 1)
+    for N, T, H, HV, dt in ((64, 2, 16, 32, "bf16"), (1, 4, 8, 8, "bf16"), (512, 8, 16, 64, "bf16"),
+                            (8, 12, 2, 2, "f32"), (32, 1, 16, 16, "bf16"), (128, 3, 16, 32, "bf16")):
+        for tile in (0, 32, 64, 128):
+            for groups in (0, 1, 2, 4):
+                for sched in (0, 1, 2):
+                    for variant in (kda.VARIANT_AUTO, kda.VARIANT_SMALL, kda.VARIANT_LARGE):
+                        p = kda.make_params(N, T, H, HV, 128, 128, dtype=dt, tile_columns=tile, column_groups=groups,
+                                            schedule=sched, variant=variant)
+                        ptrs, wsb = _fake_ptrs(p)
+                        if _validate(lib, p, ptrs, wsb) != 0:
+                            continue
+                        got = kda.select_launch(p)
+                        key = (got["tile_columns"], got["column_groups"])
+                        assert key in BUILT_128, (N, T, H, HV, dt, tile, groups, sched, variant, got)
+                        if dt == "f32" and T > 8:
+                            assert got["tile_columns"] < 128
+                        if got["schedule"] == 2:
+                            assert got["tile_columns"] == 128
 
 
 def test_prepared_call_checks_arguments_once():

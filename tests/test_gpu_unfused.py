@@ -11,7 +11,7 @@ import torch
 import linear_attention_decode_kda_amd as kda
 import oracle
 from linear_attention_decode_kda_amd import synth
-from gpu_util import assert_matches, run_gpu, say, slice_inputs, to_dev
+from gpu_util import assert_matches, assert_matches_all, run_gpu, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,7 @@ def test_unfused_close_to_fused_at_full_size():
     assert torch.equal(a["conv_window"], b["conv_window"]) and torch.equal(a["conv_state"], b["conv_state"])
     assert (a["inter_ssm"] - b["inter_ssm"]).abs().max().item() <= 2e-3
     assert (a["o"].float() - b["o"].float()).abs().max().item() <= 2e-3
+    assert_matches_all(w, inp, b, what="unfused gva")
 
 
 def test_unfused_rejects_the_queue_schedule():
@@ -70,6 +71,4 @@ def test_unfused_rejects_the_queue_schedule():
         run_unfused(w, inp, schedule=2)
     assert kda.select_launch(kda.params_for(w))["schedule"] == 2
     got = run_unfused(w, inp)
-    sample = np.array([0, w.N - 1])
-    ref = oracle.verify_workload(w.with_(N=2), slice_inputs(inp, sample))
-    assert_matches(w, got, ref, n_index=sample, what="unfused, AUTO")
+    assert_matches_all(w, inp, got, what="unfused, AUTO")
