@@ -134,7 +134,9 @@ def bit_view(t: torch.Tensor) -> torch.Tensor:
 
 
 def checksums(t: torch.Tensor, row: int) -> torch.Tensor:
-    """Per-row int64 sums of the raw bits of ``t`` (rows of ``row`` elements, on the GPU):
-    a positional fingerprint that any changed bit pattern alters, computed in one read."""
-    b = bit_view(t).reshape(-1, row)
-    return b.sum(dim=1, dtype=torch.int64)
+    """Per-row sums of the raw bits of ``t`` (rows of ``row`` elements, on the GPU), taken
+    as 64-bit words (wrapping): a positional fingerprint that a change of any one element's
+    bits alters, computed in one read with no temporary copy of ``t``. ``row`` elements
+    must span a multiple of 8 bytes."""
+    assert (row * t.element_size()) % 8 == 0 and t.is_contiguous()
+    return t.reshape(-1).view(torch.int64).reshape(-1, row * t.element_size() // 8).sum(dim=1)
