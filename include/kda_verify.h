@@ -17,8 +17,10 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers (hipMalloc'd or from a caching allocator) unless
- *     said otherwise. The caller owns every buffer; the library keeps no pointer
- *     after a call returns and allocates no device memory.
+ *     said otherwise. The caller owns every buffer it passes; the library keeps no
+ *     pointer to them after a call returns and allocates no device memory (the
+ *     counters of kda_conv_verify_decode_noalloc are a static array that is loaded
+ *     with the library).
  *   - Arrays are dense, row-major and contiguous. Every device base pointer must be
  *     16-byte aligned (KDA_ERR_ALIGN otherwise).
  *   - Calls are asynchronous on `stream` (NULL = the default stream); none blocks the
@@ -45,7 +47,9 @@ typedef enum {
   KDA_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
   KDA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kda_workspace_bytes() */
   KDA_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
-  KDA_ERR_ALIAS = -7        /* a written buffer overlaps another buffer */
+  KDA_ERR_ALIAS = -7,       /* a written buffer overlaps another buffer */
+  KDA_ERR_SCRATCH = -8      /* kda_conv_verify_decode_noalloc: the shape needs more counter
+                               words than its static scratch holds */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -240,6 +244,28 @@ kda_status kda_verify_commit(const kda_verify_params* p, const kda_pool_desc* po
                              const int32_t* accepted, const float* inter_ssm,
                              const void* conv_window, float* state, void* conv_state,
                              hipStream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. kda_conv_verify_decode without a
+ * workspace argument: the counters it needs (kda_workspace_bytes(p) bytes) live in a
+ * static device array of the library, KDA_NOALLOC_SCRATCH_BYTES on each GPU the library
+ * runs on, held until the process ends. Shapes that need more (N * H + 2 counter words
+ * beyond it, e.g. N * H > 65534) return KDA_ERR_SCRATCH before any HIP call. Each call
+ * first clears the counter words it uses with a small fill kernel on `stream` (no memset
+ * node, so the call can be captured in a graph), then runs the same kernels as
+ * kda_conv_verify_decode, with the same launch choice, results and validation; it calls
+ * no allocating routine. The first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress, with the device current). Every call on a GPU shares its
+ * array: calls that overlap on one GPU (two streams, two host threads) race on the
+ * counters and may return wrong results, so a caller serialises them on one stream or
+ * uses kda_conv_verify_decode with a workspace per stream. If the fill kernel launched
+ * and the step's launch then fails, KDA_ERR_LAUNCH is returned after that fill. */
+#define KDA_NOALLOC_SCRATCH_BYTES 262144
+kda_status kda_conv_verify_decode_noalloc(const kda_verify_params* p, const void* mixed_qkv,
+                                          const void* conv_weight, void* conv_state, const void* gate,
+                                          const float* A_log, const float* dt_bias, const void* beta,
+                                          const float* state, void* o, float* inter_ssm, void* conv_window,
+                                          hipStream_t stream);
 
 /* Static text for a kda_status value (never NULL). */
 const char* kda_status_string(int32_t status);

@@ -26,11 +26,13 @@ KDA_OK = 0
 STATUS = {
     0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNSUPPORTED",
     -4: "KDA_ERR_ALIGN", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_LAUNCH", -7: "KDA_ERR_ALIAS",
+    -8: "KDA_ERR_SCRATCH",
 }
 F32, BF16 = 0, 1
 GATE_SOFTPLUS, GATE_SAFE = 0, 1
 VARIANT_AUTO, VARIANT_SMALL, VARIANT_LARGE = 0, 1, 2
 MAX_T = 16
+NOALLOC_SCRATCH_BYTES = 262144  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class Params(ctypes.Structure):
@@ -97,6 +99,8 @@ def load() -> ctypes.CDLL:
     lib.kda_conv_verify_decode_pooled.restype = ctypes.c_int
     lib.kda_conv_verify_decode_unfused.argtypes = [PP, PD] + [_VP] * 13 + [_SZ, _VP]
     lib.kda_conv_verify_decode_unfused.restype = ctypes.c_int
+    lib.kda_conv_verify_decode_noalloc.argtypes = [PP] + [_VP] * 11 + [_VP]
+    lib.kda_conv_verify_decode_noalloc.restype = ctypes.c_int
     lib.kda_verify_commit.argtypes = [PP, PD] + [_VP] * 5 + [_VP]
     lib.kda_verify_commit.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int32]
@@ -234,6 +238,29 @@ def kda_conv_verify_decode(p: Params, mixed_qkv, conv_weight, conv_state, gate, 
                                        _stream(stream))
     if st != KDA_OK:
         raise KdaError(st, "kda_conv_verify_decode")
+
+
+def kda_conv_verify_decode_noalloc(p: Params, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta,
+                                   state, o, inter_ssm, conv_window, stream=None) -> None:
+    """``kda_conv_verify_decode`` without a workspace: the library keeps the counters in a
+    static per-GPU array (see include/kda_verify.h). Calls that overlap on one GPU race."""
+    N, T, H, HV, K, V = p.N, p.T, p.H, p.HV, p.K, p.V
+    C = 2 * H * K + HV * V
+    dt = _TORCH_DT.get(p.in_dtype)
+    if dt is None:
+        raise KdaError(-3, "kda_conv_verify_decode_noalloc")
+    for name, t, shape, tdt in (("mixed_qkv", mixed_qkv, (N, T, C), dt), ("conv_weight", conv_weight, (C, 4), dt),
+                                ("conv_state", conv_state, (N, C, 3), dt), ("gate", gate, (N, T, HV, K), dt),
+                                ("A_log", A_log, (HV,), torch.float32), ("dt_bias", dt_bias, (HV * K,), torch.float32),
+                                ("beta", beta, (N, T, HV), dt), ("state", state, (N, HV, K, V), torch.float32),
+                                ("o", o, (N, T, HV, V), dt), ("inter_ssm", inter_ssm, (N, T, HV, K, V), torch.float32),
+                                ("conv_window", conv_window, (N, T, C, 3), dt)):
+        _check(name, t, shape, tdt)
+    ptrs = [t.data_ptr() for t in (mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o,
+                                   inter_ssm, conv_window)]
+    st = load().kda_conv_verify_decode_noalloc(ctypes.byref(p), *[_VP(x) for x in ptrs], _VP(_stream(stream)))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_conv_verify_decode_noalloc")
 
 
 class PreparedVerify:

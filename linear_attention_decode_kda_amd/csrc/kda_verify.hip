@@ -47,11 +47,18 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_verify.h"
 #define KDA_HOST_DEVICE __host__ __device__
 #include "kda_queue.h"
+
+// Counters of kda_conv_verify_decode_noalloc (the allocation-free entry point): one copy
+// per GPU, held until the process ends. Host code never names this array in a kernel
+// argument or a copy (on the host the name is only a stand-in): it uses the device address
+// that hipGetSymbolAddress returns for the current device (kda::scratch_on_current_device).
+static __device__ __align__(256) uint32_t scratch[KDA_NOALLOC_SCRATCH_BYTES / 4];
 
 namespace kda {
 
@@ -1120,6 +1127,42 @@ LaunchFn pick_launch(const kda_verify_params* p, Tile tl, bool pre) {
   return pre ? pick<uint32_t, 1>(p->K, p->V, tl, p->T) : pick<uint32_t, 0>(p->K, p->V, tl, p->T);
 }
 
+// Device address of this GPU's copy of `scratch`, looked up once per device with that
+// device current and kept for later calls.
+hipError_t scratch_on_current_device(uint32_t** out) {
+  constexpr int kMaxDevices = 64;
+  struct Slot {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    uint32_t* ptr = nullptr;
+  };
+  static Slot slots[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  Slot& sl = slots[dev];
+  std::call_once(sl.once, [&sl] {
+    void* ptr = nullptr;
+    sl.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    sl.ptr = static_cast<uint32_t*>(ptr);
+  });
+  if (sl.err != hipSuccess) return sl.err;
+  if (!sl.ptr) return hipErrorInvalidSymbol;
+  *out = sl.ptr;
+  return hipSuccess;
+}
+
+// Zero `words` counters on `stream` with the fill kernel (never a memset node).
+hipError_t launch_zero_words(uint32_t* p, size_t words, hipStream_t stream) {
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks == 0) return hipSuccess;
+  void* args[] = {&p, &words};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&zero_words), dim3((unsigned)blocks), dim3(256), args, 0,
+                         stream);
+}
+
 bool supported_kv(int K, int V) { return K == V && (K == 16 || K == 64 || K == 128); }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -1516,16 +1559,30 @@ kda_status kda_workspace_reset(void* workspace, size_t bytes, hipStream_t stream
   if (bytes == 0) return KDA_OK;
   if (!workspace) return KDA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(workspace) & 3u) || (bytes & 3u)) return KDA_ERR_ALIGN;
-  const size_t words = bytes / 4;
-  size_t blocks = (words + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
-  uint32_t* wp = static_cast<uint32_t*>(workspace);
-  size_t n = words;
-  void* args[] = {&wp, &n};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&zero_words), dim3((unsigned)blocks), dim3(256), args, 0,
-                         stream) == hipSuccess
-             ? KDA_OK
-             : KDA_ERR_LAUNCH;
+  return launch_zero_words(static_cast<uint32_t*>(workspace), bytes / 4, stream) == hipSuccess ? KDA_OK
+                                                                                              : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_conv_verify_decode_noalloc(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,
+                                          void* conv_state, const void* gate, const float* A_log,
+                                          const float* dt_bias, const void* beta, const float* state, void* o,
+                                          float* inter_ssm, void* conv_window, hipStream_t stream) {
+  kda_status st = check_params(p);
+  if (st != KDA_OK) return st;
+  const size_t need = kda_workspace_bytes(p);
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+  if (p->N == 0) return KDA_OK;
+  uint32_t* ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
+  PoolView pv;
+  st = validate_verify(p, nullptr, &pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o,
+                       inter_ssm, conv_window, ws, KDA_NOALLOC_SCRATCH_BYTES);
+  if (st != KDA_OK) return st;
+  // the counters must start at zero; the previous call on this GPU normally left them so,
+  // but one that did not run to completion may not have
+  if (launch_zero_words(ws, need / 4, stream) != hipSuccess) return KDA_ERR_LAUNCH;
+  return launch_verify(p, pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta, state, o, inter_ssm,
+                       conv_window, ws, stream, false);
 }
 
 const char* kda_status_string(int32_t status) {
@@ -1538,6 +1595,7 @@ const char* kda_status_string(int32_t status) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
     case KDA_ERR_ALIAS: return "an output buffer overlaps another buffer";
+    case KDA_ERR_SCRATCH: return "the shape needs more counters than the allocation-free call's static scratch holds";
     default: return "unknown status";
   }
 }

@@ -128,6 +128,22 @@ def test_zero_sequences_is_a_no_op(lib):
     assert lib.kda_conv_verify_decode(ctypes.byref(p), *null, 0, None) == 0
 
 
+def test_noalloc_size_limit_and_params_checked_before_any_hip_call(lib):
+    """The allocation-free entry point refuses shapes whose counters exceed its static
+    scratch, and invalid params, on the host (no GPU here: a HIP call would fail)."""
+    p = kda.make_params(4096, 1, 16, 16, 128, 128)  # 65536 + 2 counter words
+    assert kda.workspace_bytes(p) > kda.NOALLOC_SCRATCH_BYTES
+    fake = [ctypes.c_void_p((i + 1) << 40) for i in range(11)]
+    assert lib.kda_conv_verify_decode_noalloc(ctypes.byref(p), *fake, None) == -8
+    p = kda.make_params(4, 0, 2, 2, 128, 128)
+    assert lib.kda_conv_verify_decode_noalloc(ctypes.byref(p), *fake, None) == -2
+    p = kda.make_params(0, 4, 2, 2, 128, 128)  # an empty batch is a no-op
+    assert lib.kda_conv_verify_decode_noalloc(ctypes.byref(p), *fake, None) == 0
+    p = kda.make_params(4094, 1, 16, 16, 128, 128)  # 65504 + 2 words: fits
+    assert kda.workspace_bytes(p) <= kda.NOALLOC_SCRATCH_BYTES
+    assert "static scratch" in kda.lib_status_string(-8)
+
+
 def test_status_strings(lib):
     for st in range(-7, 1):
         s = lib.kda_status_string(st).decode()
