@@ -164,161 +164,130 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
     }
 
 
-def sweep(out_path: str, quick: bool = False, hs=None, heads_per_qk: int = 1, ts=None, units=None) -> None:
-    """H = HV x T x N sweep over every tile width, snapshot store policy and workgroups-per-CU
-    cap on the grid schedule, whole-V workgroups in 2 or 4 column groups on the uncapped grid
-    and in 2 at one per CU, and the queue schedule of whole-V workgroups at one per CU in 1, 2 or 4 column groups
-    (K = V = 128, bf16, softplus). Buffer sets are rotated so that
-    at least 1 GiB is touched between reuses (small shapes would otherwise run from the
-    256 MB last-level cache). A cap is timed only where the grid has more workgroups than
-    the cap lets run at once, the queue only where there are more units than CUs.
-    heads_per_qk > 1 gives each q/k head that many value heads (HV = heads_per_qk H); units =
-    (lo, hi) keeps only the shapes with lo <= N HV <= hi. Writes one JSON object per shape to
-    out_path and prints a summary line."""
+def sweep_launches() -> dict:
+    """The launches the dispatch sweep times on every shape (K = V = 128), by name: the
+    32-column split; whole-V grids without a cap in 1, 2 or 4 column groups, each unit
+    order (o1 XCD ranges, o2 pairs) and store policy (s1 streaming, s2 streaming at device
+    scope); capped grids (one or two workgroups per CU; 64 columns at two per CU); and the
+    queue at one workgroup per CU in 1, 2 or 4 column groups."""
+    L = {"split32 s1": dict(tile_columns=32, max_wg_per_cu=8, store_policy=1, unit_order=1)}
+    for g in (1, 2, 4):
+        for st in (1, 2):
+            for o in (1, 2):
+                L[f"grid g{g} s{st} o{o}"] = dict(tile_columns=128, max_wg_per_cu=8, column_groups=g,
+                                                  store_policy=st, unit_order=o)
+    for g in (1, 2):
+        for st in (1, 2):
+            L[f"cap1 g{g} s{st}"] = dict(tile_columns=128, max_wg_per_cu=1, column_groups=g, store_policy=st,
+                                         unit_order=1)
+    for st in (1, 2):
+        L[f"cap2 g1 s{st}"] = dict(tile_columns=128, max_wg_per_cu=2, store_policy=st, unit_order=1)
+        L[f"cap2 64c s{st}"] = dict(tile_columns=64, max_wg_per_cu=2, store_policy=st, unit_order=1)
+    for g in (1, 2, 4):
+        for st in (1, 2):
+            L[f"queue g{g} s{st}"] = dict(tile_columns=128, max_wg_per_cu=1, column_groups=g, store_policy=st,
+                                          schedule=2)
+    return L
+
+
+def launch_name(ln: dict) -> str:
+    """The sweep's name for a launch reported by select_launch."""
+    if ln["schedule"] == 2:
+        return f"queue g{ln['column_groups']} s{ln['store_policy']}"
+    if ln["tile_columns"] == 32:
+        return f"split32 s{ln['store_policy']}"
+    if ln["max_wg_per_cu"]:
+        if ln["tile_columns"] == 64:
+            return f"cap{ln['max_wg_per_cu']} 64c s{ln['store_policy']}"
+        return f"cap{ln['max_wg_per_cu']} g{ln['column_groups']} s{ln['store_policy']}"
+    if ln["tile_columns"] == 64:
+        return f"grid 64c s{ln['store_policy']}"
+    return f"grid g{ln['column_groups']} s{ln['store_policy']} o{ln['unit_order']}"
+
+
+def sweep(out_path: str, hs, gs, ts, ns, units_range, rounds: int = 2) -> None:
+    """Dispatch sweep (K = V = 128, bf16, softplus gate): on every shape H x (HV = g H) x T x
+    N with units = N HV inside units_range, each launch of sweep_launches() and AUTO's own
+    launch, round-robin over `rounds` rounds. In each round a launch gets one untimed pass
+    over the shape's buffer sets and then a median over >= 8 timed calls (HIP events); the
+    buffer sets rotate so that >= 1 GiB is touched between reuses of a set. A cap is timed
+    only where it binds (more workgroups than cap x 256 CUs), the queue only from 512 units,
+    the 32-column split only up to 512 units. One JSON object per shape: the mean over the
+    rounds of each launch's median time, and AUTO's launch."""
     import torch
 
     import linear_attention_decode_kda_amd as kda
     from linear_attention_decode_kda_amd import synth
 
     dev = torch.device("cuda:0")
-    Hs = tuple(hs) if hs else (8, 32) if quick else (8, 16, 32, 64)
-    Ts = tuple(ts) if ts else (2, 4, 8) if quick else (1, 2, 4, 6, 8)
-    Ns = (1, 8, 64, 256) if quick else (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
-    combos = [(t, pol, occ, 1, 1) for t in (32, 64, 128) for pol in (1, 2) for occ in (8, 6, 4, 2, 1)]
-    combos += [(128, pol, 8, g, 1) for pol in (1, 2) for g in (2, 4)]
-    combos += [(128, pol, 1, 2, 1) for pol in (1, 2)]
-    combos += [(128, pol, 1, g, 2) for pol in (1, 2) for g in (1, 2, 4)]
-    rows = []
+    launches = sweep_launches()
     with open(out_path, "w") as f:
-        for H in Hs:
-            for T in Ts:
-                for N in Ns:
-                    HV = heads_per_qk * H
-                    if units and not units[0] <= N * HV <= units[1]:
-                        continue
-                    w = synth.Workload(f"sweep", N=N, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16",
-                                       gate="softplus", seed=1)
-                    b_alg = synth.algorithmic_bytes(w)
-                    nset = max(1, min(16, (1 << 30) // b_alg + 1))
-                    sets = []
-                    for _ in range(nset):
-                        inp = {
-                            "mixed_qkv": torch.randn(N, T, w.C, device=dev).to(torch.bfloat16),
-                            "conv_weight": (torch.randn(w.C, 4, device=dev) * 0.5).to(torch.bfloat16),
-                            "conv_state": torch.randn(N, w.C, 3, device=dev).to(torch.bfloat16),
-                            "gate": torch.randn(N, T, HV, 128, device=dev).to(torch.bfloat16),
-                            "A_log": torch.rand(HV, device=dev),
-                            "dt_bias": torch.randn(HV * 128, device=dev) * 0.1,
-                            "beta": torch.randn(N, T, HV, device=dev).to(torch.bfloat16),
-                            "state": torch.randn(N, HV, 128, 128, device=dev) * 0.1,
-                        }
-                        sets.append((inp, kda.alloc_outputs(w, dev)))
-                    res = {}
-                    for tile, pol, occ, g, sched in combos + [(0, 0, 0, 0, 0)]:
-                        if tile and occ < 8 and N * HV * (128 // tile) <= 256 * occ:
-                            continue  # the cap would not bind, or no unit would come from the queue
-                        p = kda.params_for(w, tile_columns=tile, store_policy=pol, max_wg_per_cu=occ,
-                                           column_groups=g, schedule=sched)
-                        ws = kda.alloc_workspace(p, dev)
-                        calls = [kda.PreparedVerify(p, a, o, ws) for a, o in sets]
-                        for i in range(2 * nset):
-                            calls[i % nset]()
-                        reps = max(8, 2 * nset)
-                        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                              for _ in range(reps)]
-                        for i in range(reps):
-                            ev[i][0].record()
-                            calls[i % nset]()
-                            ev[i][1].record()
-                        torch.cuda.synchronize()
-                        ms = sorted(a.elapsed_time(b) for a, b in ev)
-                        key = f"{tile}/{pol}" + (f"/{occ}" if occ < 8 else "") + (f" g{g}" if g > 1 else "") + (
-                            " q" if sched == 2 else "")
-                        res[key if tile else "auto"] = ms[len(ms) // 2]
-                    best = min((v, k) for k, v in res.items() if k != "auto")
-                    auto_p = kda.params_for(w)
-                    row = {"H": H, "HV": HV, "T": T, "N": N, "units": N * HV, "bytes": b_alg, "ms": res,
-                           "best": best[1], "best_pct": 100 * b_alg / best[0] / 1e6 / HBM_PEAK_GBPS,
-                           "auto_variant": kda.select_variant(auto_p),
-                           "auto_over_best": res["auto"] / best[0]}
-                    rows.append(row)
-                    f.write(json.dumps(row) + "\n")
-                    f.flush()
-                    print(f"H={H:3d} HV={HV:3d} T={T} N={N:4d} units={N * HV:6d} best={best[1]:7s} "
-                          f"{row['best_pct']:5.1f}% auto/best={row['auto_over_best']:.3f}", flush=True)
-                    del sets
-                    torch.cuda.empty_cache()
-    worst = max(rows, key=lambda r: r["auto_over_best"])
-    print(f"auto within {100 * (worst['auto_over_best'] - 1):.1f}% of the best combo on every shape "
-          f"(worst: H={worst['H']} T={worst['T']} N={worst['N']})", flush=True)
-
-
-def sweep_store(out_path: str) -> None:
-    """Snapshot store policy sweep: on each shape, AUTO's launch (tile, cap, column groups,
-    schedule) with the streaming stores (policy 1) and the device-scope streaming stores
-    (policy 2), timed alternately. Shapes: T = 1..8, 256..32768 (sequence, value head)
-    units, q/k heads shared by 1 or 2 value heads (H = 16, K = V = 128, bf16, softplus),
-    buffers rotated so that >= 1 GiB is touched between reuses. One JSON object per shape."""
-    import torch
-
-    import linear_attention_decode_kda_amd as kda
-    from linear_attention_decode_kda_amd import synth
-
-    dev = torch.device("cuda:0")
-    H = 16
-    with open(out_path, "w") as f:
-        for g in (1, 2):
-            HV = H * g
-            for T in range(1, 9):
-                for units in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
-                    N = units // HV
-                    w = synth.Workload("sweep_store", N=N, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16",
-                                       gate="softplus", seed=1)
-                    b_alg = synth.algorithmic_bytes(w)
-                    nset = max(2, min(16, (1 << 30) // b_alg + 1))
-                    sets = []
-                    for _ in range(nset):
-                        inp = {
-                            "mixed_qkv": torch.randn(N, T, w.C, device=dev).to(torch.bfloat16),
-                            "conv_weight": (torch.randn(w.C, 4, device=dev) * 0.5).to(torch.bfloat16),
-                            "conv_state": torch.randn(N, w.C, 3, device=dev).to(torch.bfloat16),
-                            "gate": torch.randn(N, T, HV, 128, device=dev).to(torch.bfloat16),
-                            "A_log": torch.rand(HV, device=dev),
-                            "dt_bias": torch.randn(HV * 128, device=dev) * 0.1,
-                            "beta": torch.randn(N, T, HV, device=dev).to(torch.bfloat16),
-                            "state": torch.randn(N, HV, 128, 128, device=dev) * 0.1,
-                        }
-                        sets.append((inp, kda.alloc_outputs(w, dev)))
-                    launch = kda.select_launch(kda.params_for(w))
-                    calls = {}
-                    for pol in (1, 2):
-                        p = kda.params_for(w, store_policy=pol)
-                        ws = kda.alloc_workspace(p, dev)
-                        calls[pol] = [kda.PreparedVerify(p, a, o, ws) for a, o in sets]
-                    # one rotation over the buffer sets for both policies: consecutive calls never
-                    # share a set, so neither policy reads what the other just left in the cache
-                    for i in range(2 * nset):
-                        for pol in (1, 2):
-                            calls[pol][(2 * i + pol) % nset]()
-                    reps = max(12, 2 * nset)
-                    ev = {pol: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                                for _ in range(reps)] for pol in (1, 2)}
-                    for i in range(reps):
-                        for pol in (1, 2):
-                            ev[pol][i][0].record()
-                            calls[pol][(2 * i + pol) % nset]()
-                            ev[pol][i][1].record()
-                    torch.cuda.synchronize()
-                    ms = {pol: sorted(a.elapsed_time(b) for a, b in ev[pol])[reps // 2] for pol in (1, 2)}
-                    pct = {pol: 100 * b_alg / ms[pol] / 1e6 / HBM_PEAK_GBPS for pol in (1, 2)}
-                    row = {"H": H, "HV": HV, "T": T, "N": N, "units": units, "bytes": b_alg, "launch": launch,
-                           "ms": ms, "pct": pct}
-                    f.write(json.dumps(row) + "\n")
-                    f.flush()
-                    print(f"g={g} T={T} units={units:6d} auto_store={launch['store_policy']} "
-                          f"nt {pct[1]:5.1f}%  nt+dev {pct[2]:5.1f}%", flush=True)
-                    del sets, calls
-                    torch.cuda.empty_cache()
+        for g in gs:
+            for H in hs:
+                HV = g * H
+                for T in ts:
+                    for N in ns:
+                        units = N * HV
+                        if not units_range[0] <= units <= units_range[1]:
+                            continue
+                        w = synth.Workload("sweep", N=N, T=T, H=H, HV=HV, K=128, V=128, dtype="bf16",
+                                           gate="softplus", seed=1)
+                        b_alg = synth.algorithmic_bytes(w)
+                        nset = max(1, min(16, (1 << 30) // b_alg + 1))
+                        sets = []
+                        for _ in range(nset):
+                            inp = {
+                                "mixed_qkv": torch.randn(N, T, w.C, device=dev).to(torch.bfloat16),
+                                "conv_weight": (torch.randn(w.C, 4, device=dev) * 0.5).to(torch.bfloat16),
+                                "conv_state": torch.randn(N, w.C, 3, device=dev).to(torch.bfloat16),
+                                "gate": torch.randn(N, T, HV, 128, device=dev).to(torch.bfloat16),
+                                "A_log": torch.rand(HV, device=dev),
+                                "dt_bias": torch.randn(HV * 128, device=dev) * 0.1,
+                                "beta": torch.randn(N, T, HV, device=dev).to(torch.bfloat16),
+                                "state": torch.randn(N, HV, 128, 128, device=dev) * 0.1,
+                            }
+                            sets.append((inp, kda.alloc_outputs(w, dev)))
+                        todo = {}
+                        for name, kw in list(launches.items()) + [("auto", {})]:
+                            cap = kw.get("max_wg_per_cu", 8)
+                            wgs = units * (128 // kw.get("tile_columns", 128))
+                            if kw.get("schedule") == 2 and units < 512:
+                                continue
+                            if kw.get("schedule") != 2 and cap < 8 and wgs <= 256 * cap:
+                                continue
+                            if kw.get("tile_columns") == 32 and units > 512:
+                                continue
+                            p = kda.params_for(w, **kw)
+                            ws = kda.alloc_workspace(p, dev)
+                            todo[name] = [kda.PreparedVerify(p, a, o, ws) for a, o in sets]
+                        times = {k: [] for k in todo}
+                        reps = max(8, nset)
+                        for _ in range(rounds):
+                            for name, calls in todo.items():
+                                for i in range(nset):
+                                    calls[i]()
+                                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                      for _ in range(reps)]
+                                for i in range(reps):
+                                    ev[i][0].record()
+                                    calls[i % nset]()
+                                    ev[i][1].record()
+                                torch.cuda.synchronize()
+                                ms = sorted(a.elapsed_time(b) for a, b in ev)
+                                times[name].append(ms[len(ms) // 2])
+                        res = {k: sum(v) / len(v) for k, v in times.items()}
+                        auto = kda.select_launch(kda.params_for(w))
+                        best = min((v, k) for k, v in res.items() if k != "auto")
+                        row = {"H": H, "HV": HV, "T": T, "N": N, "units": units, "bytes": b_alg, "ms": res,
+                               "auto": auto, "auto_name": launch_name(auto), "best": best[1],
+                               "auto_over_best": res["auto"] / best[0]}
+                        f.write(json.dumps(row) + "\n")
+                        f.flush()
+                        print(f"H={H:3d} HV={HV:3d} T={T} N={N:4d} units={units:6d} best={best[1]:16s} "
+                              f"{100 * b_alg / best[0] / 1e6 / HBM_PEAK_GBPS:5.1f}% auto={row['auto_name']:16s} "
+                              f"auto/best={row['auto_over_best']:.3f}", flush=True)
+                        del sets, todo
+                        torch.cuda.empty_cache()
 
 
 def main():
@@ -339,18 +308,21 @@ def main():
     ap.add_argument("--groups", type=int, default=0, help="override: column groups of a whole-V workgroup (1, 2, 4)")
     ap.add_argument("--schedule", type=int, default=0,
                     help="override: 1 one workgroup per unit, 2 resident workgroups pulling units from a queue")
+    ap.add_argument("--order", type=int, default=0,
+                    help="override: unit order of the grid, 1 XCD ranges, 2 pairs of units dealt to the XCDs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
-                    help="run the H x T x N sweep over tile widths and store policies instead")
-    ap.add_argument("--sweep-quick", action="store_true", help="a reduced sweep grid")
-    ap.add_argument("--sweep-store", default=None, metavar="OUT.jsonl",
-                    help="time AUTO's launch with store policy 1 and 2 over T x units x shared heads")
-    ap.add_argument("--sweep-h", default="", help="comma-separated H values for --sweep (default all)")
-    ap.add_argument("--sweep-g", type=int, default=1, help="value heads per q/k head for --sweep (HV = g H)")
-    ap.add_argument("--sweep-t", default="", help="comma-separated T values for --sweep (default 1,2,4,6,8)")
-    ap.add_argument("--sweep-units", default="", metavar="LO,HI",
+                    help="run the dispatch sweep (every launch of sweep_launches() and AUTO's on each shape) "
+                         "instead of the benchmark")
+    ap.add_argument("--sweep-h", default="8,16,32,64", help="comma-separated H values for --sweep")
+    ap.add_argument("--sweep-g", default="1,2", help="comma-separated value heads per q/k head for --sweep")
+    ap.add_argument("--sweep-t", default="1,2,3,4,6,8", help="comma-separated T values for --sweep")
+    ap.add_argument("--sweep-n", default="2,4,6,8,12,16,24,32,48,64,96,128,192,256",
+                    help="comma-separated N values for --sweep")
+    ap.add_argument("--sweep-units", default="128,4096", metavar="LO,HI",
                     help="keep only the --sweep shapes with LO <= N HV <= HI units")
+    ap.add_argument("--sweep-rounds", type=int, default=2, help="round-robin rounds per shape for --sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -369,12 +341,9 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.sweep:
-        sweep(args.sweep, args.sweep_quick, [int(x) for x in args.sweep_h.split(",") if x], args.sweep_g,
-              [int(x) for x in args.sweep_t.split(",") if x],
-              tuple(int(x) for x in args.sweep_units.split(",")) if args.sweep_units else None)
-        return
-    if args.sweep_store:
-        sweep_store(args.sweep_store)
+        ints = lambda x: [int(v) for v in x.split(",") if v]  # noqa: E731
+        sweep(args.sweep, ints(args.sweep_h), ints(args.sweep_g), ints(args.sweep_t), ints(args.sweep_n),
+              tuple(ints(args.sweep_units)), args.sweep_rounds)
         return
 
     if args.copy_calibration:
@@ -390,7 +359,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     variant = {"auto": kda.VARIANT_AUTO, "small": kda.VARIANT_SMALL, "large": kda.VARIANT_LARGE}[args.variant]
     p = kda.params_for(w, variant=variant, tile_columns=args.tile, store_policy=args.store,
-                       max_wg_per_cu=args.occ, column_groups=args.groups, schedule=args.schedule)
+                       max_wg_per_cu=args.occ, column_groups=args.groups, schedule=args.schedule,
+                       unit_order=args.order)
     resolved = {kda.VARIANT_SMALL: "small", kda.VARIANT_LARGE: "large"}[kda.select_variant(p)]
     print(f"[bench] workload={w.name} N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V} "
           f"{w.dtype} {w.gate} variant={resolved}", file=sys.stderr, flush=True)

@@ -109,6 +109,12 @@ typedef struct {
                                variant) and the fused step (the unfused form rejects it).
                                0: the AUTO choice with the AUTO tile, the grid with a
                                caller's tile */
+  int32_t unit_order;       /* grid schedule only: the order in which units are dealt to
+                               the 8 XCDs (workgroups go to them round-robin). 1 XCD ranges:
+                               each XCD takes one contiguous range of units; 2 pairs: pairs
+                               of neighbouring units go to the XCDs in turn. 0: pairs when
+                               whole-V workgroups run without a cap (all resident at once),
+                               XCD ranges otherwise */
 } kda_verify_params;
 
 #define KDA_MAX_T 16
@@ -137,12 +143,13 @@ int32_t kda_select_variant(const kda_verify_params* p);
 
 /* The launch configuration kda_conv_verify_decode would use for these params (after the
  * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 streaming at
- * device scope),
- * workgroups-per-CU cap (0 = none), column groups per workgroup and schedule (1 grid,
- * 2 queue). Host-only; any output pointer may be NULL. Returns the params' validation
- * status (outputs untouched unless KDA_OK). */
+ * device scope), workgroups-per-CU cap (0 = none), column groups per workgroup, schedule
+ * (1 grid, 2 queue) and unit order (1 XCD ranges, 2 pairs; the queue takes its first
+ * round in XCD ranges). Host-only; any output pointer may be NULL. Returns the params'
+ * validation status (outputs untouched unless KDA_OK). */
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
-                             int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule);
+                             int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule,
+                             int32_t* unit_order);
 
 /* Validate params and pointers without launching (host-only, no HIP call). */
 kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,

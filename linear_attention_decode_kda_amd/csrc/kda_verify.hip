@@ -155,14 +155,28 @@ __device__ __forceinline__ void store_snapshot(float* p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
 
-// Workgroups are handed to the 8 XCDs round-robin by blockIdx. Map blockIdx so that
-// each XCD works through one contiguous range of units: the WGs sharing an XCD's L2 then
-// stream through neighbouring state and snapshot addresses. A bijection on [0, B).
+// Workgroups are handed to the 8 XCDs round-robin by blockIdx. Two orders of units over
+// them, both bijections on [0, B):
+//  * XCD ranges: each XCD works through one contiguous range of units, so the WGs sharing
+//    an XCD's L2 stream through neighbouring state and snapshot addresses. Measured best
+//    when a grid runs in several generations of workgroups (per-CU caps).
+//  * pairs: pairs of neighbouring units are dealt to the XCDs in turn (units 2x and 2x + 1
+//    of every 16 go to XCD x). Measured best when every workgroup of the grid is resident
+//    at once: then all of them write the same token's snapshots at the same time, and
+//    spreading each XCD's share over the whole batch sped those calls up by 1-9 % (the
+//    512-unit four-token call by 11 %).
+constexpr int kNXcd = 8;
 __device__ __forceinline__ int xcd_order(int b, int B) {
-  constexpr int NXCD = 8;
-  const int x = b % NXCD, q = B / NXCD, r = B % NXCD;
-  return x * q + (x < r ? x : r) + b / NXCD;
+  const int x = b % kNXcd, q = B / kNXcd, r = B % kNXcd;
+  return x * q + (x < r ? x : r) + b / kNXcd;
 }
+__device__ __forceinline__ int pair_order(int b, int B) {
+  constexpr int P = 2 * kNXcd;  // units per round of pairs
+  if (b >= B - B % P) return b;  // the last partial round keeps its place
+  const int x = b % kNXcd, i = b / kNXcd;
+  return (i >> 1) * P + 2 * x + (i & 1);
+}
+enum UnitOrder { kOrderXcdRanges = 1, kOrderPairs = 2 };
 
 // ----------------------------------------------------------------------------------
 // kernel arguments
@@ -188,6 +202,7 @@ struct Args {
   int N, T, H, HV, C;
   int g;      // HV / H
   int group;  // WGs reading one q/k head's conv cache: g * (V-tiles)
+  int order;  // UnitOrder of the grid schedule
   int gate_mode;
   float lower_bound, softplus_beta, softplus_threshold, scale, eps;
 };
@@ -736,7 +751,8 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
 template <class CF, typename R>
 __global__ __launch_bounds__(CF::NTHR) void kda_verify_kernel(const Args a) {
   __shared__ Smem<CF, R> s;
-  verify_unit<CF, R, false>(a, s, xcd_order(blockIdx.x, gridDim.x), 0);
+  const int b = blockIdx.x, B = gridDim.x;
+  verify_unit<CF, R, false>(a, s, a.order == kOrderPairs ? pair_order(b, B) : xcd_order(b, B), 0);
 }
 
 // Queue schedule: only as many workgroups as are resident at once. Each takes one unit
@@ -888,6 +904,7 @@ struct Tile {
   int occ = 0;         // workgroups per CU cap (lds_reservation), 0 = none
   int g = 1;           // column groups of 4 waves sharing the WG's staging and conv
   bool queue = false;  // resident workgroups pulling units from a counter (whole-V only)
+  int order = kOrderXcdRanges;  // UnitOrder of the grid
 };
 using LaunchFn = hipError_t (*)(const Args&, const Tile&, hipStream_t);
 
@@ -932,6 +949,7 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
   const long long units = (long long)a.N * a.HV * CF::NVT;
   Args copy = a;
   copy.group = a.g * CF::NVT;
+  copy.order = tl.order;
   void* args[] = {&copy};
   const size_t want = lds_reservation(tl.occ), have = sizeof(Smem<CF, R>);
   const size_t dyn = want > have ? want - have : 0;
@@ -949,96 +967,39 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
                          dim3(CF::NTHR), args, dyn, stream);
 }
 
-// Tile shape, workgroups-per-CU cap, column groups and schedule, from sweeps on MI355X
-// (K = V = 128, bf16; every combination timed on each shape, buffers rotated so that each
-// run reads and writes HBM): H = HV x T x N over 200 shapes, GVA shapes (HV = 2H, 4H),
-// column groups on 179 shapes of 1024-32768 units, and the queue schedule against the grid
-// on 105 shapes of 2048-32768 units. The choice per bucket is the one with the best mean.
-// A cap limits how many workgroups stream snapshots at once: from a thousand units up, one
-// whole-V workgroup per CU keeps HBM busiest. From a few thousand units the queue schedule
-// (one resident workgroup per CU pulling units) beats launching a workgroup per unit by
-// 2-14 %: the XCDs no longer finish their fixed shares at different times, and no
-// workgroup launch sits between two units of a CU. Below that the queue's first round is
-// most of the work and its counter traffic does not pay.
-//   queue, one WG per CU: T = 1 without shared q/k heads from 2048 units, in four column
-//     groups; T = 2 from 4096 units, and from 2048 without shared heads (+1.4-5.6 %), in
-//     two column groups; T = 3-5 from 2048 units and T >= 6 from 2560, in one (with the
-//     device-scope streaming stores: +2-7 % at T = 3; at T = 4-8, timed against the grid
-//     on 2048 and 3072 units with 16-256 sequences, +2-10 % at 3072, +1.6 and +2.1 % on
-//     average at T = 4 and 5 on 2048, where T = 6-8 gain nothing and lose up to 3 % at
-//     T = 8 with many sequences);
-//   otherwise the grid. Below 1024 units (a sweep of 100 shapes of 128-768 units, T = 1-8,
-//     three timings each), where one generation of workgroups is most of the call and
-//     shorter per-unit chains pay:
-//     <= 64 units, and <= 128 at T = 2: the 32-column split (4 WGs per unit);
-//     <= 128 units: whole V in four column groups; 129-447: whole V in two column groups
-//     (T = 1: four below 320 units, else one; T = 3, 5, 7 from 256 units: one group; the
-//     store policy there in auto_store_128); 448-512: whole V;
-//     513-1023: whole V at T <= 2, else one WG per CU in two groups;
-//   from 1024 units, whole V: T <= 2: two WGs per CU (64 columns at T = 2 from 2048);
-//     T <= 5: one WG per CU in two column groups; T >= 6: one WG per CU, with shared q/k
-//     heads in two column groups below 2048 units.
-// Every tile width, grouping and schedule uses the same K split (32 rows per wave) and the
-// same partial-sum tree, so all of them return bit-identical results; the cap and the
-// schedule only change which CU runs a unit, and when.
-Tile auto_shape_128(long long units, int T, int g) {
-  // queue schedule, one whole-V workgroup per CU
-  if (T == 1 && g == 1 && units >= 2048) return Tile{128, kStoreNT, 1, 4, true};
-  if ((T >= 2 && units >= 4096) || (T == 2 && g == 1 && units >= 2048) || (T >= 3 && T <= 5 && units >= 2048) ||
-      (T >= 6 && units >= 2560)) {
-    if (T == 2) return Tile{128, kStoreNT, 1, 2, true};
-    return Tile{128, kStoreNT, 1, 1, true};
-  }
-  // the grid: below 1024 units
+// AUTO launch for K = V = 128, from two dispatch sweeps on MI355X (bench.py --sweep, two
+// boxes: 486 shapes with H = 8-64 and 399 with H = 12, 24, 48, one or two value heads per
+// q/k head, T = 1-8, 128-4096 (sequence, value head) units; 27 launches each, timed
+// round-robin over rotated buffer sets). Five buckets:
+//   1. <= 64 units (<= 128 at T = 2): the 32-column split, four workgroups per unit, so that
+//      a launch-latency-bound call spreads over more CUs;
+//   2. <= 512 units, one generation of whole-V workgroups (all resident at once, no cap):
+//      four column groups up to 128 units and at T = 1 up to 256 (a 16-wave workgroup runs
+//      one per CU, so 256 of them are one generation); one group at T = 1 beyond that, from
+//      448 units, and at odd T from 256 units; two groups otherwise. Streaming stores
+//      (policy 1) at T = 2 and 4 and with four groups, device scope (policy 2) otherwise;
+//   3. T = 1, or < 1024 units, or < 2048 units at T = 2: the uncapped whole-V grid;
+//   4. < 2048 units at T = 3, 4: two whole-V workgroups per CU;
+//   5. otherwise the queue, one whole-V workgroup per CU, two column groups at T = 2.
+// Buckets 3-5 store at device scope. The unit order follows from the launch (choose_tile):
+// pairs for uncapped whole-V grids. Every launch uses the same K split (32 rows per wave)
+// and partial-sum tree, so all return bit-identical results; cap, schedule and order only
+// change which CU runs a unit, and when.
+Tile auto_tile_128(long long units, int T) {
   if (units <= 64 || (units <= 128 && T == 2)) return Tile{32, kStoreNT};
-  if (units <= 128) return Tile{128, kStoreNT, 0, 4};
-  if (units < 448) {
-    if (units >= 256 && (T == 3 || T == 5 || T == 7)) return Tile{128, kStoreNT};  // see auto_store_128
-    return Tile{128, kStoreNT, 0, T > 1 ? 2 : units < 320 ? 4 : 1};
+  if (units <= 512) {
+    int g;
+    if (units <= 128 || (T == 1 && units <= 256))
+      g = 4;
+    else if (T == 1 || units >= 448 || (T % 2 == 1 && units >= 256))
+      g = 1;
+    else
+      g = 2;
+    return Tile{128, (T == 2 || T == 4 || g == 4) ? kStoreNT : kStoreNTDev, 0, g};
   }
-  if (units <= 512) return Tile{128, kStoreNT};
-  if (units < 1024) return T <= 2 ? Tile{128, kStoreNT} : Tile{128, kStoreNT, 1, 2};
-  // the grid from 1024 units
-  if (T <= 2) return T == 2 && units >= 2048 ? Tile{64, kStoreNT, 2} : Tile{128, kStoreNT, 2};
-  if (T <= 5) return Tile{128, kStoreNT, 1, 2};
-  if (g > 1 && units < 2048) return Tile{128, kStoreNT, 1, 2};
-  return Tile{128, kStoreNT, 1};
-}
-
-// Snapshot store policy for AUTO's launch, from a sweep that timed AUTO's launch with both
-// policies on 128 shapes (T = 1-8, 256-32768 units, q/k heads shared by 1 or 2 value
-// heads; H = 16), the two alternating over distinct buffer sets so that neither reads what
-// the other left in the last-level cache, and refreshed sweeps of every launch combination
-// (HV = H and HV = 2H). The device-scope streaming stores win by 1-8 points of HBM peak
-// from 8192 units at T >= 2, on the queue from 2048 units at T >= 3 (2-4 % over the plain
-// streaming stores on that queue), at T = 1 from 1024 units, at T = 2 on 1024-2047 units,
-// and at T >= 6 on grids of 512-2047 units (with shared q/k heads below 1024, where the
-// two-group launch is otherwise mixed). On grids of 256-447 units at
-// T = 3-8 (repeated sweeps at 256 units with HV = 8-64 and at 384 units with HV = 12-48):
-// at T = 3, 5 and 7, one whole-V group with the device-scope stores beat two groups with
-// the plain streaming stores (+1-4 % at T = 3, 0-4 % at T = 5, +2-8 % at T = 7); at even T
-// the two-group launch gains from the device-scope stores (+1.4 % at T = 6 with HV a power
-// of two; +1.4-5.2 % at T = 4, 6, 8 with HV = 12, 24, 48) except where a sequence's
-// snapshots span a power of two (T HV 64 KiB; T = 4, 8 with HV a power of two: -0.3 to
-// -0.9 %). Elsewhere the two policies are within noise or the plain streaming stores win.
-int auto_store_128(long long units, int T, int g, int HV) {
-  if (T == 1) return units >= 1024 ? kStoreNTDev : kStoreNT;
-  if (units >= 256 && units < 448 && T >= 3 && T <= 8) {
-    const long long span = (long long)T * HV;  // snapshot rows of one sequence, in units of 64 KiB
-    if (T % 2 == 1 || (span & (span - 1)) != 0) return kStoreNTDev;
-  }
-  if (T >= 3 && units >= 2048) return kStoreNTDev;  // the queue, or the capped grid at T >= 6
-  if (units >= 8192) return kStoreNTDev;
-  if (units >= 4096) return T >= 4 ? kStoreNTDev : kStoreNT;
-  if (T == 2 && units >= 1024 && units < 2048) return kStoreNTDev;
-  if (T >= 6 && units >= 512 && (g == 1 || units < 1024 || units >= 2048)) return kStoreNTDev;
-  return kStoreNT;
-}
-
-Tile auto_tile_128(long long units, int T, int g, int HV) {
-  Tile t = auto_shape_128(units, T, g);
-  t.stp = auto_store_128(units, T, g, HV);
-  return t;
+  if (T == 1 || units < 1024 || (units < 2048 && T == 2)) return Tile{128, kStoreNTDev};
+  if (units < 2048 && T <= 4) return Tile{128, kStoreNTDev, 2};
+  return Tile{128, kStoreNTDev, 1, T == 2 ? 2 : 1, true};
 }
 
 // The AUTO choice with the caller's overrides applied. A cap belongs to the AUTO tile: when
@@ -1049,7 +1010,7 @@ Tile choose_tile(const kda_verify_params* p) {
   const bool caller_tile = p->tile_columns != 0 || p->variant != KDA_VARIANT_AUTO;
   Tile t;
   if (K == 128 && V == 128) {
-    t = auto_tile_128((long long)p->N * p->HV, p->T, p->HV / p->H, p->HV);
+    t = auto_tile_128((long long)p->N * p->HV, p->T);
     if (caller_tile) {
       t.occ = 0;
       t.g = 1;
@@ -1077,6 +1038,12 @@ Tile choose_tile(const kda_verify_params* p) {
   if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu == 8 ? 0 : p->max_wg_per_cu;
   if (p->column_groups != 0) t.g = p->column_groups;
   if (p->schedule != 0) t.queue = p->schedule == 2;
+  // unit order of the grid: pairs when whole-V workgroups run without a cap (every
+  // workgroup resident at once), XCD ranges otherwise
+  if (p->unit_order != 0)
+    t.order = p->unit_order;
+  else
+    t.order = t.vt == V && t.occ == 0 && !t.queue ? kOrderPairs : kOrderXcdRanges;
   return t;
 }
 
@@ -1201,6 +1168,7 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
   p->max_wg_per_cu = 0;
   p->column_groups = 0;
   p->schedule = 0;
+  p->unit_order = 0;
 }
 
 static kda_status check_params(const kda_verify_params* p) {
@@ -1235,6 +1203,7 @@ static kda_status check_params(const kda_verify_params* p) {
     if (!ok) return KDA_ERR_UNSUPPORTED;
   }
   if (p->schedule < 0 || p->schedule > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->unit_order < 0 || p->unit_order > 2) return KDA_ERR_UNSUPPORTED;
   if (p->schedule == 2) {
     // the queue runs whole-V workgroups
     bool ok = true;
@@ -1265,7 +1234,8 @@ int32_t kda_select_variant(const kda_verify_params* p) {
 }
 
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
-                             int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule) {
+                             int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule,
+                             int32_t* unit_order) {
   const kda_status st = check_params(p);
   if (st != KDA_OK) return st;
   const Tile t = choose_tile(p);
@@ -1274,6 +1244,7 @@ kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, 
   if (max_wg_per_cu) *max_wg_per_cu = t.occ;
   if (column_groups) *column_groups = t.g;
   if (schedule) *schedule = t.queue ? 2 : 1;
+  if (unit_order) *unit_order = t.order;
   return KDA_OK;
 }
 
@@ -1434,6 +1405,7 @@ kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const v
   a.C = 2 * p->H * p->K + p->HV * p->V;
   a.g = p->HV / p->H;
   a.group = 0;
+  a.order = kOrderXcdRanges;
   a.gate_mode = p->gate_mode;
   a.lower_bound = p->lower_bound;
   a.softplus_beta = p->softplus_beta;

@@ -3,8 +3,7 @@
   python -m linear_attention_decode_kda_amd.rocprof_summary stats <kernel_stats.csv> <cmd> <out.md>
   python -m linear_attention_decode_kda_amd.rocprof_summary traffic <workload> <variant>
          <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <cmd-file> <out.json>
-  python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md <sweep.jsonl> <cmd> <out.md> [refs]
-  python -m linear_attention_decode_kda_amd.rocprof_summary store-md <sweep_store.jsonl> <cmd> <out.md>
+  python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md <sweep.jsonl> <cmd> <out.md>
 
 `traffic` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the verify
 kernel by what the same counters read for a plain 1 GiB device copy (read 1 GiB, write
@@ -45,34 +44,6 @@ def stats(csv_path: str, cmd: str, out: str) -> None:
         short = name if len(name) < 110 else name[:107] + "..."
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    with open(out, "w") as f:
-        f.write("\n".join(lines) + "\n")
-
-
-def store_md(jsonl: str, cmd: str, out: str) -> None:
-    """Table of the store-policy sweep (bench.py --sweep-store) with the policy the library's
-    AUTO rule picks for each shape now (host-only call, no GPU)."""
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-    import linear_attention_decode_kda_amd as kda
-
-    rows = [json.loads(l) for l in open(jsonl) if l.strip()]
-    lines = ["# Snapshot store policy sweep (K = V = 128, bf16, softplus gate, H = 16)", "",
-             f"Command: `{cmd}`", "",
-             "AUTO's launch (tile, cap, column groups, schedule) timed with the streaming stores (1: `nt`) and "
-             "the streaming stores at device scope (2: `nt sc1`), alternately over distinct buffer sets (>= 1 GiB "
-             "touched between reuses of a set); median of >= 12 calls each. Percent of the 8 TB/s HBM peak = "
-             "algorithmic bytes / kernel time. `AUTO` is the policy the library picks for the shape.", "",
-             "| value heads per q/k head | T | units | 1: nt % | 2: nt sc1 % | AUTO |", "|---|---|---|---|---|---|"]
-    gain = []
-    for r in rows:
-        g = r["HV"] // r["H"]
-        p = kda.make_params(r["N"], r["T"], r["H"], r["HV"], 128, 128)
-        auto = kda.select_launch(p)["store_policy"]
-        p1, p2 = r["pct"]["1"], r["pct"]["2"]
-        gain.append((max(p1, p2) - (p1 if auto == 1 else p2)))
-        lines.append(f"| {g} | {r['T']} | {r['units']} | {p1:.1f} | {p2:.1f} | {auto} |")
-    lines += ["", f"AUTO's pick is within {max(gain):.1f} points of the faster policy on every shape "
-              f"(mean {statistics.mean(gain):.2f} points)."]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -118,45 +89,56 @@ def traffic(workload, variant, fetch, write, cfetch, cwrite, cmd_file, out) -> N
         f.write("\n")
 
 
-def sweep_md(jsonl: str, cmd: str, out: str, refs: str = "") -> None:
-    """Table of a `bench.py --sweep` run: per shape the best (tile/store[/cap]) and its
-    share of the HBM peak, the AUTO choice and its share, and reference launches (refs,
-    comma-separated combination labels; four by default)."""
+def _bucket(units: int) -> str:
+    return ("<= 128" if units <= 128 else "129-512" if units <= 512 else "513-1023" if units < 1024
+            else "1024-2047" if units < 2048 else ">= 2048")
+
+
+def sweep_md(jsonl: str, cmd: str, out: str) -> None:
+    """Table of a `bench.py --sweep` run (the dispatch sweep): per shape the fastest launch
+    and its share of the HBM peak, the launch AUTO ran at the time of the sweep, and the
+    launch the library's rule picks now (host-only call) with its time over the fastest."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
     import linear_attention_decode_kda_amd as kda
 
     rows = [json.loads(ln) for ln in open(jsonl) if ln.strip()]
-    pct = lambda r, k: 100.0 * r["bytes"] / r["ms"][k] / 1e6 / 8000.0 if k in r["ms"] else float("nan")
-    refs = tuple(refs.split(",")) if refs else ("32/1", "128/1", "128/1/1", "128/1/1 q")
-    g = rows[0].get("HV", rows[0]["H"]) // rows[0]["H"]
-    title = "H = HV" if g == 1 else f"H, HV = {g} H"
-    lines = [f"# {title} x T x N sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
-             f"Command: `{cmd}` (one MI355X; each shape's buffers rotated so that >= 1 GiB is touched "
-             "between reuses; median of >= 8 calls per combination), summarised by "
+    pct = lambda r, ms: 100.0 * r["bytes"] / ms / 1e6 / 8000.0  # noqa: E731
+    lines = [f"# Dispatch sweep of the verify kernel (K = V = 128, bf16, softplus gate)", "",
+             f"Command: `{cmd}` (one MI355X), summarised by "
              f"`python -m linear_attention_decode_kda_amd.rocprof_summary sweep-md {os.path.basename(jsonl)} ...`.",
              "",
-             "Combinations are tile/store[/cap][ gN][ q]: V columns per workgroup, snapshot store policy "
-             "(1 streaming, 2 the library's policy 2 at the time of the run), the workgroups-per-CU cap (none, 6, 4, 2, 1; a cap is timed "
-             "only where the grid has more workgroups than it lets run at once), column groups of a "
-             "whole-V workgroup (gN), and q for the queue schedule (resident workgroups pulling units; "
-             "otherwise one workgroup per unit). Percent of the 8 TB/s HBM "
-             "peak = algorithmic bytes / kernel time. Shapes of <= 128 units are launch-latency-bound: "
-             "their timings include the launch, and the columns differ by noise.", "",
-             "| H | HV | T | N | units | best | best % | AUTO | AUTO % | AUTO/best | " + " | ".join(refs) + " |",
-             "|---|---|---|---|---|---|---|---|---|---|" + "---|" * len(refs)]
+             "Every shape's launches were timed round-robin (each: an untimed pass over the buffer sets, then the "
+             "median of >= 8 calls from HIP events, in each of two rounds; the mean of the rounds), over buffer "
+             "sets rotated so that >= 1 GiB is touched between reuses of a set. Launch names: `split32` the "
+             "32-column split; `grid gG` whole-V workgroups without a cap in G column groups; `capC` at most C "
+             "workgroups per CU (`64c`: 64 columns); `queue gG` one resident workgroup per CU pulling units; "
+             "`s1` streaming stores, `s2` streaming at device scope; `o1` XCD-range unit order, `o2` pairs. "
+             "Percent of the 8 TB/s HBM peak = algorithmic bytes / time (launch gap included). `rule` is the "
+             "launch the library picks now; `rule/best` its time over the fastest launch.", "",
+             "| H | HV | T | N | units | fastest | % | AUTO at the time | rule now | rule % | rule/best |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    regs, per = [], {}
     for r in rows:
-        p = kda.make_params(r["N"], r["T"], r["H"], r.get("HV", r["H"]), 128, 128)
-        ln = kda.select_launch(p)
-        auto = (f"{ln['tile_columns']}/{ln['store_policy']}" + (f"/{ln['max_wg_per_cu']}" if ln["max_wg_per_cu"] else "")
-                + (f" g{ln['column_groups']}" if ln["column_groups"] > 1 else "")
-                + (" q" if ln.get("schedule") == 2 else ""))
-        lines.append(f"| {r['H']} | {r.get('HV', r['H'])} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | "
-                     f"{r['best_pct']:.1f} | {auto} | "
-                     f"{pct(r, 'auto'):.1f} | {r['auto_over_best']:.3f} | "
-                     + " | ".join(f"{pct(r, k):.1f}" if k in r["ms"] else "-" for k in refs) + " |")
-    mean = statistics.mean(r["auto_over_best"] for r in rows)
-    big = [r for r in rows if r["units"] >= 256]
-    lines += ["", f"AUTO over best, mean over all {len(rows)} shapes: {mean:.3f}; over the {len(big)} shapes "
-              f"of >= 256 units: {statistics.mean(r['auto_over_best'] for r in big):.3f}."]
+        best_ms = min(v for k, v in r["ms"].items() if k != "auto")
+        ln = kda.select_launch(kda.make_params(r["N"], r["T"], r["H"], r["HV"], 128, 128))
+        name = bench.launch_name(ln)
+        ms = r["ms"].get(name)
+        if ms is None and name == r.get("auto_name"):
+            ms = r["ms"].get("auto")
+        reg = ms / best_ms if ms else float("nan")
+        if ms:
+            regs.append(reg)
+            per.setdefault(_bucket(r["units"]), []).append(reg)
+        lines.append(f"| {r['H']} | {r['HV']} | {r['T']} | {r['N']} | {r['units']} | {r['best']} | "
+                     f"{pct(r, best_ms):.1f} | {r.get('auto_name', '-')} | {name} | "
+                     f"{pct(r, ms) if ms else float('nan'):.1f} | {reg:.3f} |")
+    lines += ["", f"Rule now over the fastest launch, over the {len(regs)} shapes whose rule launch was timed: mean "
+              f"{statistics.mean(regs):.3f}, worst {max(regs):.3f}.", "",
+              "| units | shapes | mean rule/best |", "|---|---|---|"]
+    for b in ("<= 128", "129-512", "513-1023", "1024-2047", ">= 2048"):
+        if b in per:
+            lines.append(f"| {b} | {len(per[b])} | {statistics.mean(per[b]):.3f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -167,8 +149,6 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10])
     elif sys.argv[1] == "sweep-md":
-        sweep_md(*sys.argv[2:6])
-    elif sys.argv[1] == "store-md":
-        store_md(*sys.argv[2:5])
+        sweep_md(*sys.argv[2:5])
     else:
         raise SystemExit(__doc__)

@@ -253,7 +253,7 @@ def test_tuning_overrides(lib):
                 dict(tile_columns=64, column_groups=2), dict(variant=kda.VARIANT_SMALL, column_groups=4),
                 dict(dtype="f32", T=12, column_groups=2), dict(schedule=3), dict(schedule=-1),
                 dict(tile_columns=64, schedule=2), dict(variant=kda.VARIANT_SMALL, schedule=2),
-                dict(dtype="f32", T=12, schedule=2)):
+                dict(dtype="f32", T=12, schedule=2), dict(unit_order=3), dict(unit_order=-1)):
         kw = dict(bad)
         p = kda.make_params(8, kw.pop("T", 4), 2, 2, 128, 128, **kw)
         ptrs, wsb = _fake_ptrs(p)
@@ -281,12 +281,12 @@ BUILT_128 = {(128, 1), (128, 2), (128, 4), (64, 1), (32, 1)}
 def test_every_accepted_override_names_a_built_launch(lib):
     """Any combination of overrides that validates resolves to a launch some kernel
     implements: column groups split whole-V workgroups only, so asking for groups without a
-    tile takes whole V even where AUTO's own tile is narrower (T = 2 with shared q/k heads
-    on 2048 units, where AUTO runs 64 columns)."""
-    p = kda.make_params(64, 2, 16, 32, 128, 128)
-    assert kda.select_launch(p)["tile_columns"] == 64
-    p = kda.make_params(64, 2, 16, 32, 128, 128, column_groups=2)
-    assert tuple(kda.select_launch(p).values()) == (128, 1, 2, 2, 1)
+    tile takes whole V even where AUTO's own tile is narrower (the 32-column split of a
+    one-sequence call)."""
+    p = kda.make_params(1, 4, 8, 8, 128, 128)
+    assert kda.select_launch(p)["tile_columns"] == 32
+    p = kda.make_params(1, 4, 8, 8, 128, 128, column_groups=2)
+    assert tuple(kda.select_launch(p).values()) == (128, 1, 0, 2, 1, 2)
     for N, T, H, HV, dt in ((64, 2, 16, 32, "bf16"), (1, 4, 8, 8, "bf16"), (512, 8, 16, 64, "bf16"),
                             (8, 12, 2, 2, "f32"), (32, 1, 16, 16, "bf16"), (128, 3, 16, 32, "bf16")):
         for tile in (0, 32, 64, 128):
@@ -323,116 +323,81 @@ def test_prepared_call_checks_arguments_once():
 
 def test_select_launch_follows_the_dispatch_rule(lib):
     """The AUTO rule (tile, stores, workgroups-per-CU cap, column groups, schedule: 1 grid,
-    2 queue) on the named workloads and at the edges of its buckets, and the overrides
+    2 queue) on the named workloads and at the edges of its five buckets, and the overrides
     winning over it."""
-    L = lambda *shape, **kw: tuple(kda.select_launch(kda.make_params(*shape, **kw)).values())
+    L = lambda *shape, **kw: tuple(kda.select_launch(kda.make_params(*shape, **kw)).values())[:5]
     assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0, 1, 1)            # tiny: the only K = V = 16 tile
     assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0, 1, 1)       # small batch: 512 units, T = 4
     assert L(64, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)       # GVA: 2048 units, T = 3
     assert L(256, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)      # large batch: 8192 units
     assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 2)      # max bandwidth: 32768 units, T = 8
-    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)           # <= 64 units: latency-bound split
+    # 1. <= 64 units, and <= 128 at T = 2: the 32-column split
+    assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)
     assert L(4, 4, 16, 16, 128, 128) == (32, 1, 0, 1, 1)
-    assert L(8, 2, 16, 16, 128, 128) == (32, 1, 0, 1, 1)         # ... and <= 128 at T = 2
-    assert L(8, 4, 16, 16, 128, 128) == (128, 1, 0, 4, 1)        # <= 128 units: four column groups
-    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 4, 1)        # 129-447 units: four groups at T = 1 ...
-    assert L(12, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... (one from 320)
-    assert L(12, 4, 32, 32, 128, 128) == (128, 1, 0, 2, 1)       # ... else two
-    assert L(8, 3, 32, 32, 128, 128) == (128, 2, 0, 1, 1)        # ... but at T = 3, 5, 7 from 256 units one,
-    assert L(13, 7, 32, 32, 128, 128) == (128, 2, 0, 1, 1)       #     with device-scope stores
-    assert L(8, 5, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
-    assert L(7, 3, 16, 32, 128, 128) == (128, 1, 0, 2, 1)        #     (224 units: two groups)
-    assert L(14, 5, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       #     (448 units: the next bucket)
-    # ... even T: device-scope stores unless a sequence's snapshots span a power of two
-    # (T HV = 128 for the two "else two" shapes above; 48, 192 and 96 here)
-    assert L(32, 4, 12, 12, 128, 128) == (128, 2, 0, 2, 1)
-    assert L(16, 8, 8, 24, 128, 128) == (128, 2, 0, 2, 1)
-    assert L(8, 6, 16, 32, 128, 128) == (128, 2, 0, 2, 1)
-    assert L(8, 9, 32, 32, 128, 128) == (128, 1, 0, 2, 1)        #     (measured up to T = 8 only)
-    assert L(16, 8, 16, 16, 128, 128) == (128, 1, 0, 2, 1)
-    assert L(24, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # 513-1023 units
-    assert L(24, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)
-    assert L(24, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(12, 8, 16, 64, 128, 128) == (128, 2, 1, 2, 1)
-    assert L(32, 1, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
-    assert L(64, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)       # T = 1 queue from 2048 units
-    assert L(64, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)       # ... not with shared q/k heads
-    assert L(512, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
-    assert L(64, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)
-    assert L(128, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2 queue from 4096 units
-    assert L(512, 2, 64, 64, 128, 128) == (128, 2, 1, 2, 2)
-    assert L(16, 4, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T <= 5
-    assert L(32, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(127, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(128, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(1024, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(63, 3, 32, 32, 128, 128) == (128, 1, 1, 2, 1)       # T = 3: the grid below 2048 units ...
-    assert L(64, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)       # ... then the queue, device-scope stores
-    assert L(128, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(256, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(128, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # ... with shared q/k heads too
-    assert L(63, 3, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(64, 3, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(512, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(128, 4, 16, 32, 128, 128) == (128, 2, 1, 1, 2)      # shared q/k heads
-    assert L(512, 4, 16, 64, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(8, 6, 32, 32, 128, 128) == (128, 2, 0, 2, 1)        # T >= 6 (256-447 units: see the span rule)
-    assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
-    assert L(64, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
-    assert L(79, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 1)       # T >= 6: the queue from 2560 units
-    assert L(80, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(32, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
-    assert L(64, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 1)
-    assert L(128, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(256, 8, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(256, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(512, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    # the edges of the store rule (2: streaming at device scope)
-    assert L(31, 1, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 1: from 1024 units ...
-    assert L(32, 1, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
-    assert L(511, 1, 32, 32, 128, 128) == (128, 2, 1, 4, 2)
-    assert L(31, 1, 16, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... also with shared q/k heads
-    assert L(256, 1, 16, 32, 128, 128) == (128, 2, 2, 1, 1)
-    assert L(63, 8, 16, 32, 128, 128) == (128, 1, 1, 2, 1)       # T >= 6, shared heads: not 1024-2047 units
-    assert L(31, 2, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T = 2: 1024-2047 units
-    assert L(32, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
-    assert L(63, 2, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
-    assert L(64, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)       # T = 2 queue from 2048 units, no sharing
-    assert L(64, 2, 16, 32, 128, 128) == (64, 1, 2, 1, 1)        # ... the grid with shared q/k heads
-    assert L(255, 2, 32, 32, 128, 128) == (128, 1, 1, 2, 2)      # T >= 2: from 8192 units
-    assert L(256, 2, 32, 32, 128, 128) == (128, 2, 1, 2, 2)
-    assert L(63, 4, 32, 32, 128, 128) == (128, 1, 1, 2, 1)       # T = 3-5: from 2048 units (the queue)
-    assert L(64, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(64, 5, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(96, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)        # 3072 units
-    assert L(15, 6, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # T >= 6: from 512 units ...
-    assert L(16, 6, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
-    assert L(63, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 1)
-    assert L(127, 6, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(16, 6, 16, 32, 128, 128) == (128, 2, 0, 1, 1)       # ... with shared q/k heads below 1024
-    assert L(32, 6, 16, 32, 128, 128) == (128, 1, 1, 2, 1)
+    assert L(8, 2, 16, 16, 128, 128) == (32, 1, 0, 1, 1)
+    # ... and four column groups up to 128 units
+    assert L(8, 4, 16, 16, 128, 128) == (128, 1, 0, 4, 1)
+    assert L(5, 7, 4, 20, 128, 128) == (128, 1, 0, 4, 1)
+    # 2. 129-512 units, no cap: groups ...
+    assert L(8, 1, 32, 32, 128, 128) == (128, 1, 0, 4, 1)        # T = 1: four up to 256 units ...
+    assert L(9, 1, 32, 32, 128, 128) == (128, 2, 0, 1, 1)        # ... one beyond
+    assert L(12, 4, 32, 32, 128, 128) == (128, 1, 0, 2, 1)       # two below 448 ...
+    assert L(14, 4, 32, 32, 128, 128) == (128, 1, 0, 1, 1)       # ... one from 448
+    assert L(7, 3, 16, 32, 128, 128) == (128, 2, 0, 2, 1)        # odd T: two below 256 units ...
+    assert L(8, 3, 32, 32, 128, 128) == (128, 2, 0, 1, 1)        # ... one from 256
+    assert L(13, 7, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(8, 6, 16, 32, 128, 128) == (128, 2, 0, 2, 1)        # even T >= 6: device-scope stores
+    assert L(16, 8, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(16, 2, 16, 16, 128, 128) == (128, 1, 0, 2, 1)       # T = 2 and 4: streaming stores
+    # 3. the uncapped grid: below 1024 units, at T = 1, and below 2048 units at T = 2
+    assert L(24, 4, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(31, 8, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(64, 1, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(512, 1, 16, 64, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(63, 2, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    # 4. two per CU below 2048 units at T = 3, 4
+    assert L(32, 3, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
+    assert L(63, 4, 16, 32, 128, 128) == (128, 2, 2, 1, 1)
+    # 5. the queue, one per CU: from 2048 units at T = 2-4, from 1024 at T >= 5
+    assert L(64, 2, 16, 32, 128, 128) == (128, 2, 1, 2, 2)
+    assert L(64, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(32, 5, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(31, 8, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
+    assert L(32, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(1024, 16, 8, 8, 128, 128) == (128, 2, 1, 1, 2)
+    # overrides
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6, 1, 1)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 2, 0, 1, 1)   # the AUTO cap goes with its tile
-    assert L(32, 4, 32, 32, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: no AUTO cap
-    assert L(32, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 1, 0, 2, 1)   # 8: explicitly none
-    assert L(32, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 1, 2, 1, 1)
-    assert L(32, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 1, 0, 1, 1)
-    assert L(32, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 1, 0, 1, 1)
-    assert L(32, 4, 32, 32, 128, 128, store_policy=2) == (128, 2, 1, 2, 1)
-    assert L(32, 4, 32, 32, 128, 128, column_groups=4) == (128, 1, 1, 4, 1)
+    assert L(32, 4, 32, 32, 128, 128, tile_columns=128) == (128, 2, 0, 1, 1)  # caller's tile: no AUTO cap
+    assert L(32, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 2, 0, 1, 1)   # 8: explicitly none
+    assert L(32, 4, 32, 32, 128, 128, tile_columns=128, max_wg_per_cu=2) == (128, 2, 2, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, variant=kda.VARIANT_SMALL) == (32, 2, 0, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, variant=kda.VARIANT_LARGE) == (128, 2, 0, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, store_policy=1) == (128, 1, 2, 1, 1)
+    assert L(32, 4, 32, 32, 128, 128, column_groups=4) == (128, 2, 2, 4, 1)
     assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2, 1, 1)
     assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 2, 1, 1, 1)      # the grid, AUTO cap kept
-    assert L(32, 4, 32, 32, 128, 128, schedule=2) == (128, 1, 1, 2, 2)
+    assert L(32, 4, 32, 32, 128, 128, schedule=2) == (128, 2, 2, 1, 2)
     assert L(1, 4, 8, 8, 128, 128, schedule=2) == (128, 1, 0, 1, 2)          # the queue takes whole V
     assert L(8, 4, 16, 16, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: one group
     assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 2, 0, 1, 2)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=128) == (128, 2, 0, 1, 1)  # caller's tile: the grid
     assert L(3, 16, 1, 4, 64, 64, schedule=2) == (64, 1, 0, 1, 2)
     # fp32 at T > 8: two 64-column workgroups, one group each, on the grid
-    assert L(64, 9, 8, 16, 128, 128, dtype="f32") == (64, 1, 1, 1, 1)
+    assert L(64, 9, 8, 16, 128, 128, dtype="f32") == (64, 2, 1, 1, 1)
     assert L(512, 9, 32, 32, 128, 128, dtype="f32") == (64, 2, 1, 1, 1)
     assert kda.make_params(1, 0, 1, 1, 128, 128) and lib.kda_select_launch(
-        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None, None, None) == -2
+        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None, None, None, None) == -2
+    # unit order: pairs for whole-V grids without a cap (every workgroup resident at once),
+    # XCD ranges for capped grids, the 32-column split and the queue; the override wins
+    O = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["unit_order"]
+    assert O(32, 4, 16, 16, 128, 128) == 2                      # small batch
+    assert O(12, 4, 32, 32, 128, 128) == 2 and O(8, 4, 16, 16, 128, 128) == 2
+    assert O(32, 3, 32, 32, 128, 128) == 1                      # capped grid
+    assert O(24, 4, 32, 32, 128, 128) == 2                      # uncapped grid of 768 units
+    assert O(256, 4, 32, 32, 128, 128) == 1 and O(1, 4, 8, 8, 128, 128) == 1
+    assert O(2, 2, 2, 2, 16, 16) == 2                           # K = V = 16: whole V, no cap
+    assert O(32, 4, 16, 16, 128, 128, unit_order=1) == 1 and O(256, 4, 32, 32, 128, 128, unit_order=2) == 2
     G = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["column_groups"]
     assert G(256, 4, 32, 32, 128, 128, column_groups=4) == 4
     assert G(256, 4, 32, 32, 128, 128, tile_columns=128) == 1     # caller's tile: one group unless asked

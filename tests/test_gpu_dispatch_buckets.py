@@ -1,8 +1,8 @@
-"""Every branch of the dispatch rule on grids of 256-447 (sequence, value head) units, on
-the GPU through the C ABI: one whole-V group with the device-scope streaming stores at odd
-T; two groups at even T, with the device-scope stores unless a sequence's snapshots span a
-power of two (T HV blocks of K V floats); value-head counts that are not powers of two
-among them (HV = 12, 24, 48).
+"""Every branch of the dispatch rule on grids of 129-2304 (sequence, value head) units, on
+the GPU through the C ABI: one generation of whole-V workgroups in one, two or four column
+groups with either store policy (129-512 units), the uncapped grid below 1024 units; value-head counts that are not powers of
+two among them (HV = 12, 24, 36, 40, 48); two workgroups per CU below 2048 units at T = 3,
+4, and the uncapped grid at T = 1 beyond 2048 units.
 
 For each shape the launch AUTO picks is pinned, its results must equal those of the
 32-column split bit for bit (every launch shares the K split and the partial-sum tree),
@@ -26,12 +26,20 @@ pytestmark = pytest.mark.gpu
 
 # (N, T, H, HV, gate) -> the launch AUTO must pick: (tile, store policy, cap, groups, schedule)
 CASES = [
-    ((16, 7, 16, 16, "softplus"), (128, 2, 0, 1, 1)),   # 256 units, odd T: one group
+    ((12, 2, 4, 12, "softplus"), (128, 1, 0, 2, 1)),    # 144 units, T = 2: two groups, streaming stores
+    ((6, 5, 4, 40, "safe"), (128, 2, 0, 2, 1)),         # 240 units, odd T below 256: two groups
+    ((16, 7, 16, 16, "softplus"), (128, 2, 0, 1, 1)),   # 256 units, odd T: one group, device scope
     ((32, 3, 12, 12, "safe"), (128, 2, 0, 1, 1)),       # 384 units, odd T, HV = 12
-    ((8, 4, 32, 32, "safe"), (128, 1, 0, 2, 1)),        # 256 units, T HV = 128: streaming stores
-    ((16, 4, 8, 24, "softplus"), (128, 2, 0, 2, 1)),    # 384 units, T HV = 96
-    ((16, 6, 8, 24, "safe"), (128, 2, 0, 2, 1)),        # 384 units, T HV = 144
-    ((8, 8, 16, 48, "softplus"), (128, 2, 0, 2, 1)),    # 384 units, T HV = 384
+    ((8, 4, 32, 32, "safe"), (128, 1, 0, 2, 1)),        # 256 units, T = 4: two groups, streaming
+    ((16, 4, 8, 24, "softplus"), (128, 1, 0, 2, 1)),    # 384 units, T = 4, HV = 24
+    ((16, 6, 8, 24, "safe"), (128, 2, 0, 2, 1)),        # 384 units, T = 6: device scope
+    ((8, 8, 16, 48, "softplus"), (128, 2, 0, 2, 1)),    # 384 units, T = 8, HV = 48
+    ((20, 1, 8, 24, "safe"), (128, 2, 0, 1, 1)),        # 480 units, T = 1: one group
+    ((24, 3, 12, 36, "softplus"), (128, 2, 0, 1, 1)),   # 864 units, T = 3: the uncapped grid
+    ((40, 4, 12, 24, "safe"), (128, 2, 0, 1, 1)),       # 960 units, T = 4: the uncapped grid
+    ((9, 1, 32, 32, "softplus"), (128, 2, 0, 1, 1)),    # 288 units, T = 1: one group beyond 256
+    ((64, 4, 12, 24, "softplus"), (128, 2, 2, 1, 1)),   # 1536 units, T = 4: two per CU
+    ((96, 1, 8, 24, "safe"), (128, 2, 0, 1, 1)),        # 2304 units, T = 1: the uncapped grid
 ]
 
 
@@ -45,7 +53,7 @@ def test_bucket_launch_and_parity(shape, launch):
     N, T, H, HV, gate = shape
     w = synth.Workload(f"bucket-N{N}-T{T}-H{H}-HV{HV}", N=N, T=T, H=H, HV=HV, K=128, V=128,
                        dtype="bf16", gate=gate, seed=7000 + 10 * T + HV)
-    assert tuple(kda.select_launch(kda.params_for(w)).values()) == launch
+    assert tuple(kda.select_launch(kda.params_for(w)).values())[:5] == launch
     inp = synth.make_inputs(w)
     x0, cs0 = inp["mixed_qkv"].clone(), inp["conv_state"].clone()
     auto = run_gpu(w, inp, kda.VARIANT_AUTO)

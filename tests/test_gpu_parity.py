@@ -242,8 +242,8 @@ def test_every_tile_shape_bit_identical(w):
                                W(3, 12, 1, 2, 128, 128, gate="safe")])   # up to 16
 def test_explicit_tile_and_store_overrides_bit_identical(w):
     """Every tile width (32, 64, 128 columns per WG), both snapshot store policies, the
-    workgroups-per-CU caps and both schedules give the same bits, for each token-count
-    template; one of them
+    workgroups-per-CU caps, both schedules and both unit orders give the same bits, for
+    each token-count template; one of them
     is checked against the oracle. (The device-scope store is inline assembly: a missing
     wait after it once let later VALU writes reach memory in place of the snapshot.)"""
     inp = synth.make_inputs(w)
@@ -259,6 +259,8 @@ def test_explicit_tile_and_store_overrides_bit_identical(w):
     for groups, pol, occ in ((1, 1, 1), (2, 2, 1), (4, 1, 8)):  # the queue schedule
         outs.append(run_gpu(w, inp, A, tile_columns=128, column_groups=groups, store_policy=pol, max_wg_per_cu=occ,
                             schedule=2))
+    for tile, order in ((128, 1), (128, 2), (32, 2), (64, 1)):  # unit orders of the grid
+        outs.append(run_gpu(w, inp, A, tile_columns=tile, unit_order=order))
     for o in outs[1:]:
         for k in ("o", "inter_ssm", "conv_window", "conv_state"):
             assert torch.equal(o[k], outs[0][k]), k
