@@ -168,8 +168,9 @@ def sweep_launches() -> dict:
     """The launches the dispatch sweep times on every shape (K = V = 128), by name: the
     32-column split; whole-V grids without a cap in 1, 2 or 4 column groups, each unit
     order (o1 XCD ranges, o2 pairs) and store policy (s1 streaming, s2 streaming at device
-    scope); capped grids (one or two workgroups per CU; 64 columns at two per CU); and the
-    queue at one workgroup per CU in 1, 2 or 4 column groups."""
+    scope); capped grids (one or two workgroups per CU; 64 columns at two per CU); the queue
+    at one workgroup per CU in 1, 2 or 4 column groups; and the stream with the next state
+    tile loaded after the conv (p1) or at the start (p2)."""
     L = {"split32 s1": dict(tile_columns=32, max_wg_per_cu=8, store_policy=1, unit_order=1)}
     for g in (1, 2, 4):
         for st in (1, 2):
@@ -187,11 +188,15 @@ def sweep_launches() -> dict:
         for st in (1, 2):
             L[f"queue g{g} s{st}"] = dict(tile_columns=128, max_wg_per_cu=1, column_groups=g, store_policy=st,
                                           schedule=2)
+    for pf in (1, 2):
+        L[f"stream s2 p{pf}"] = dict(tile_columns=128, store_policy=2, schedule=3, prefetch=pf)
     return L
 
 
 def launch_name(ln: dict) -> str:
     """The sweep's name for a launch reported by select_launch."""
+    if ln["schedule"] == 3:
+        return f"stream s{ln['store_policy']} p{ln['prefetch']}"
     if ln["schedule"] == 2:
         return f"queue g{ln['column_groups']} s{ln['store_policy']}"
     if ln["tile_columns"] == 32:
@@ -211,7 +216,8 @@ def sweep(out_path: str, hs, gs, ts, ns, units_range, rounds: int = 2) -> None:
     launch, round-robin over `rounds` rounds. In each round a launch gets one untimed pass
     over the shape's buffer sets and then a median over >= 8 timed calls (HIP events); the
     buffer sets rotate so that >= 1 GiB is touched between reuses of a set. A cap is timed
-    only where it binds (more workgroups than cap x 256 CUs), the queue only from 512 units,
+    only where it binds (more workgroups than cap x 256 CUs), the queue and the stream only
+    from 512 units (the stream up to T = 8),
     the 32-column split only up to 512 units. One JSON object per shape: the mean over the
     rounds of each launch's median time, and AUTO's launch."""
     import torch
@@ -251,9 +257,11 @@ def sweep(out_path: str, hs, gs, ts, ns, units_range, rounds: int = 2) -> None:
                         for name, kw in list(launches.items()) + [("auto", {})]:
                             cap = kw.get("max_wg_per_cu", 8)
                             wgs = units * (128 // kw.get("tile_columns", 128))
-                            if kw.get("schedule") == 2 and units < 512:
+                            if kw.get("schedule", 0) >= 2 and units < 512:
                                 continue
-                            if kw.get("schedule") != 2 and cap < 8 and wgs <= 256 * cap:
+                            if kw.get("schedule") == 3 and T > 8:
+                                continue
+                            if kw.get("schedule", 0) < 2 and cap < 8 and wgs <= 256 * cap:
                                 continue
                             if kw.get("tile_columns") == 32 and units > 512:
                                 continue
@@ -307,7 +315,10 @@ def main():
     ap.add_argument("--occ", type=int, default=0, help="override: at most 1, 2, 4 or 6 workgroups per CU (8: no cap)")
     ap.add_argument("--groups", type=int, default=0, help="override: column groups of a whole-V workgroup (1, 2, 4)")
     ap.add_argument("--schedule", type=int, default=0,
-                    help="override: 1 one workgroup per unit, 2 resident workgroups pulling units from a queue")
+                    help="override: 1 one workgroup per unit, 2 resident workgroups pulling units from a queue, "
+                         "3 the queue with a producer wave loading the next unit into LDS")
+    ap.add_argument("--prefetch", type=int, default=0,
+                    help="override (schedule 3): load the next state tile 1 after the conv, 2 at the start")
     ap.add_argument("--order", type=int, default=0,
                     help="override: unit order of the grid, 1 XCD ranges, 2 pairs of units dealt to the XCDs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -360,7 +371,7 @@ def main():
     variant = {"auto": kda.VARIANT_AUTO, "small": kda.VARIANT_SMALL, "large": kda.VARIANT_LARGE}[args.variant]
     p = kda.params_for(w, variant=variant, tile_columns=args.tile, store_policy=args.store,
                        max_wg_per_cu=args.occ, column_groups=args.groups, schedule=args.schedule,
-                       unit_order=args.order)
+                       unit_order=args.order, prefetch=args.prefetch)
     resolved = {kda.VARIANT_SMALL: "small", kda.VARIANT_LARGE: "large"}[kda.select_variant(p)]
     print(f"[bench] workload={w.name} N={w.N} T={w.T} H={w.H} HV={w.HV} K={w.K} V={w.V} "
           f"{w.dtype} {w.gate} variant={resolved}", file=sys.stderr, flush=True)

@@ -107,6 +107,11 @@ typedef struct {
                                needs whole-V workgroups (with K = V = 128: tile 128, not
                                fp32 inputs at T > 8; with K = V = 64: not the SMALL
                                variant) and the fused step (the unfused form rejects it).
+                               3 stream: the queue with a fifth wave per workgroup that
+                               loads each unit's inputs and state tile into LDS while the
+                               other four compute the unit before it; K = V = 128, whole-V
+                               workgroups of one column group, one per compute unit, T <= 8,
+                               the fused step.
                                0: the AUTO choice with the AUTO tile, the grid with a
                                caller's tile */
   int32_t unit_order;       /* grid schedule only: the order in which units are dealt to
@@ -115,6 +120,11 @@ typedef struct {
                                of neighbouring units go to the XCDs in turn. 0: pairs when
                                whole-V workgroups run without a cap (all resident at once),
                                XCD ranges otherwise */
+  int32_t prefetch;         /* stream schedule only (ignored otherwise): when a workgroup
+                               loads its next unit's state tile. 1 once the current unit's
+                               conv phase is done; 2 as soon as the compute waves hold the
+                               current unit's state in registers. 0: 2 at T >= 3 up to
+                               65536 snapshot tiles (N * HV * T) per call, 1 otherwise */
 } kda_verify_params;
 
 #define KDA_MAX_T 16
@@ -144,12 +154,13 @@ int32_t kda_select_variant(const kda_verify_params* p);
 /* The launch configuration kda_conv_verify_decode would use for these params (after the
  * overrides): V columns per workgroup, snapshot store policy (1 streaming, 2 streaming at
  * device scope), workgroups-per-CU cap (0 = none), column groups per workgroup, schedule
- * (1 grid, 2 queue) and unit order (1 XCD ranges, 2 pairs; the queue takes its first
- * round in XCD ranges). Host-only; any output pointer may be NULL. Returns the params'
- * validation status (outputs untouched unless KDA_OK). */
+ * (1 grid, 2 queue, 3 stream), unit order (1 XCD ranges, 2 pairs; the queue and the
+ * stream take their first round in XCD ranges) and the stream's state prefetch (1, 2;
+ * 0 for the other schedules). Host-only; any output pointer may be NULL. Returns the
+ * params' validation status (outputs untouched unless KDA_OK). */
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
                              int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule,
-                             int32_t* unit_order);
+                             int32_t* unit_order, int32_t* prefetch);
 
 /* Validate params and pointers without launching (host-only, no HIP call). */
 kda_status kda_validate(const kda_verify_params* p, const void* mixed_qkv, const void* conv_weight,

@@ -46,7 +46,7 @@ class Params(ctypes.Structure):
         ("softplus_threshold", ctypes.c_float), ("scale", ctypes.c_float), ("l2norm_eps", ctypes.c_float),
         ("tile_columns", ctypes.c_int32), ("store_policy", ctypes.c_int32),
         ("max_wg_per_cu", ctypes.c_int32), ("column_groups", ctypes.c_int32), ("schedule", ctypes.c_int32),
-        ("unit_order", ctypes.c_int32),
+        ("unit_order", ctypes.c_int32), ("prefetch", ctypes.c_int32),
     ]
 
 
@@ -89,7 +89,7 @@ def load() -> ctypes.CDLL:
     lib.kda_select_variant.argtypes = [PP]
     lib.kda_select_variant.restype = ctypes.c_int32
     I32P = ctypes.POINTER(ctypes.c_int32)
-    lib.kda_select_launch.argtypes = [PP, I32P, I32P, I32P, I32P, I32P, I32P]
+    lib.kda_select_launch.argtypes = [PP, I32P, I32P, I32P, I32P, I32P, I32P, I32P]
     lib.kda_select_launch.restype = ctypes.c_int
     lib.kda_validate.argtypes = [PP] + [_VP] * 12 + [_SZ]
     lib.kda_validate.restype = ctypes.c_int
@@ -121,7 +121,8 @@ def make_params(N: int, T: int, H: int, HV: int, K: int, V: int, *, dtype: str =
                 gate: str = "softplus", variant: int = VARIANT_AUTO, lower_bound: float = -5.0,
                 softplus_beta: float = 1.0, softplus_threshold: float = 20.0, scale: float = 0.0,
                 l2norm_eps: float = 1e-6, tile_columns: int = 0, store_policy: int = 0,
-                max_wg_per_cu: int = 0, column_groups: int = 0, schedule: int = 0, unit_order: int = 0) -> Params:
+                max_wg_per_cu: int = 0, column_groups: int = 0, schedule: int = 0, unit_order: int = 0,
+                prefetch: int = 0) -> Params:
     p = Params()
     load().kda_verify_params_init(ctypes.byref(p), N, T, H, HV, K, V)
     p.in_dtype = {"f32": F32, "bf16": BF16}[dtype]
@@ -138,6 +139,7 @@ def make_params(N: int, T: int, H: int, HV: int, K: int, V: int, *, dtype: str =
     p.column_groups = column_groups
     p.schedule = schedule
     p.unit_order = unit_order
+    p.prefetch = prefetch
     return p
 
 
@@ -157,14 +159,15 @@ def select_variant(p: Params) -> int:
 def select_launch(p: Params) -> Dict[str, int]:
     """The launch configuration the library picks for ``p``: tile_columns, store_policy
     (1 streaming, 2 streaming at device scope), max_wg_per_cu (0 = no cap), column_groups, schedule
-    (1 grid, 2 queue) and unit_order (1 XCD ranges, 2 pairs)."""
-    t, s, o, g, q, u = (ctypes.c_int32() for _ in range(6))
+    (1 grid, 2 queue, 3 stream), unit_order (1 XCD ranges, 2 pairs) and prefetch (the stream's
+    state load: 1 after the conv, 2 at the start; 0 for the other schedules)."""
+    t, s, o, g, q, u, f = (ctypes.c_int32() for _ in range(7))
     st = load().kda_select_launch(ctypes.byref(p), ctypes.byref(t), ctypes.byref(s), ctypes.byref(o),
-                                  ctypes.byref(g), ctypes.byref(q), ctypes.byref(u))
+                                  ctypes.byref(g), ctypes.byref(q), ctypes.byref(u), ctypes.byref(f))
     if st != KDA_OK:
         raise KdaError(st, "kda_select_launch")
     return {"tile_columns": t.value, "store_policy": s.value, "max_wg_per_cu": o.value,
-            "column_groups": g.value, "schedule": q.value, "unit_order": u.value}
+            "column_groups": g.value, "schedule": q.value, "unit_order": u.value, "prefetch": f.value}
 
 
 def _stream(stream) -> int:

@@ -203,6 +203,7 @@ struct Args {
   int g;      // HV / H
   int group;  // WGs reading one q/k head's conv cache: g * (V-tiles)
   int order;  // UnitOrder of the grid schedule
+  int prefetch;  // stream schedule: StatePrefetch
   int gate_mode;
   float lower_bound, softplus_beta, softplus_threshold, scale, eps;
 };
@@ -341,7 +342,7 @@ struct alignas(16) Smem {
   // raw conv window of every token, laid out as its output row: [t][local channel][3]
   alignas(16) R win[CF::PRE ? 8 : CF::TMAX * CF::NCH * 3];
   alignas(16) float dtb[CF::K];
-  R bs[CF::TMAX];
+  uint32_t bs[CF::TMAX];  // raw beta of each token, widened to 32 bits (bf16 in the low half)
   int last;
   uint32_t next[2];  // queue schedule: the ticket for the next unit, by iteration parity
 };
@@ -359,130 +360,26 @@ __device__ __forceinline__ int gchan(int lc, int h, int H, int hv, int vt) {
   return 2 * H * CF::K + hv * CF::V + vt * CF::WT + (lc - 2 * CF::K);
 }
 
-// One (sequence, value head, V-tile) unit of the step, by the whole workgroup. Under the
-// queue schedule (QUEUE) thread 0 also takes a ticket for the workgroup's next unit as
-// the unit starts and leaves it in s.next[slot] before the first barrier.
-template <class CF, typename R, bool QUEUE>
-__device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const int lb, const int slot) {
-  constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
-  constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
+// Where a unit sits: its sequence, value head, q/k head, V-tile, and its pool rows (conv
+// cache; snapshots and windows).
+struct UnitAt {
+  int n, hv, h, vt, cs_row, in_row;
+};
 
+// Phases 1a and 1b of a unit, from the inputs staged in LDS: conv + SiLU of every staged
+// channel (and the raw windows left for the copies), then the decay and beta of each token.
+template <class CF, typename R>
+__device__ __forceinline__ void conv_and_gates(const Args& a, Smem<CF, R>& s, const bool qk_owner, const float alog) {
+  constexpr int K = CF::K, NCH = CF::NCH, NTHR = CF::NTHR;
   const int tid = threadIdx.x;
-  // The ticket is drawn by thread 0 and read only by thread 0, on the same path, so no
-  // other lane ever reads it. It gets no initial value on purpose: one would make the
-  // compiler set the register at the top of every unit, and that write waits first for
-  // every store of the previous unit still in flight (measured; a zero, an empty asm
-  // defining it and __builtin_nondeterministic_value all do).
-  uint32_t ticket;
-  if constexpr (QUEUE)
-    if (tid == 0)
-      ticket = __hip_atomic_fetch_add(a.counters + (size_t)a.N * a.H, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int wave = tid >> 6, lane = tid & 63;
-  const int T = a.T, H = a.H, HV = a.HV, C = a.C;
+  const int T = a.T;
   __builtin_assume(T >= 1 && T <= CF::TMAX);
-  const int vt = lb % CF::NVT;
-  const int unit = lb / CF::NVT;  // n * HV + hv
-  const int hv = unit % HV, n = unit / HV;
-  const int h = hv / a.g;
-  // pool rows of this sequence: conv cache, state, and the snapshot / window pools
-  const int cs_row = a.cs_idx ? a.cs_idx[n] : n;
-  const int st_row = a.st_idx ? a.st_idx[n] : n;
-  const int in_row = a.in_idx ? a.in_idx[n] : n;
-  if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
-      in_row >= a.in_slots) {
-    // padding entry: the whole unit (and its group) skips, nothing is read or written
-    if constexpr (QUEUE)
-      if (tid == 0) s.next[slot] = ticket;
-    return;
-  }
-
-  const typename CF::XR* __restrict__ xq = static_cast<const typename CF::XR*>(a.mixed_qkv);
-  const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
-  R* cstate = static_cast<R*>(a.conv_state);
-  const R* __restrict__ gq = static_cast<const R*>(a.gate);
-  const R* __restrict__ bq = static_cast<const R*>(a.beta);
-
-  // ---------------- prologue: issue every 16-byte load of the WG's small inputs
-  const int PA = NCH / CF::XE16;
-  const int nA = T * PA;              // new tokens
-  const int nB = CF::PRE ? 0 : 3 * NCH / E16;  // conv cache
-  const int nC = CF::PRE ? 0 : 4 * NCH / E16;  // conv taps
-  const int nD = T * K / E16;         // gate
-  const int nE = K / 4;               // dt_bias (fp32)
-  const int total = nA + nB + nC + nD + nE;
-  u32x4 vals[CF::MAXC];
-  int dsts[CF::MAXC];
-  char* lds = reinterpret_cast<char*>(&s);
-  const float alog = a.A_log[hv];
-  // Every slot loads unconditionally (a slot past the end re-reads the last vector and
-  // is not stored), so the loads issue back to back with no wait between them.
-#pragma unroll
-  for (int k = 0; k < CF::MAXC; ++k) {
-    const int cv = tid + k * NTHR;
-    int ci = cv < total ? cv : total - 1;
-    const void* src;
-    int dst;
-    if (ci < nA) {
-      const int t = ci / PA, pe = (ci - t * PA) * CF::XE16;
-      src = xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt);
-      dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
-    } else if ((ci -= nA) < nB) {
-      const int e = ci * E16, lc = e / 3;
-      src = cstate + ((size_t)cs_row * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
-      dst = (int)((char*)&s.cs[e] - lds);
-    } else if ((ci -= nB) < nC) {
-      const int e = ci * E16, lc = e / 4;
-      src = wq + (size_t)gchan<CF>(lc, h, H, hv, vt) * 4 + (e - lc * 4);
-      dst = (int)((char*)&s.ws[e] - lds);
-    } else if ((ci -= nC) < nD) {
-      const int e = ci * E16, t = e / K;
-      src = gq + ((size_t)(n * T + t) * HV + hv) * K + (e - t * K);
-      dst = (int)((char*)&s.gs[e] - lds);
-    } else {
-      ci -= nD;
-      src = a.dt_bias + (size_t)hv * K + ci * 4;
-      dst = (int)((char*)&s.dtb[ci * 4] - lds);
-    }
-    vals[k] = *reinterpret_cast<const u32x4*>(src);
-    dsts[k] = cv < total ? dst : -1;
-  }
-  const R bval = bq[(size_t)(n * T + (tid < T ? tid : T - 1)) * HV + hv];
-
-  // ---------------- state tile: 16-byte loads, left in flight through the prologue math
-  const int grp = wave / CF::NW, wv = wave - grp * CF::NW;  // column group, wave in the group
-  const int c4 = lane % LPR, qq = lane / LPR;
-  const int col = vt * CF::WT + grp * VT + c4 * 4;
-  const int row0 = wv * CF::RW + qq;  // this lane's rows: row0 + Q * r
-  const size_t KV = (size_t)K * V;
-  const float* sp = a.state + ((size_t)st_row * HV + hv) * KV + (size_t)row0 * V + col;
-  f32x4 S[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r)
-    S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)r * Q * V));
-
-#pragma unroll
-  for (int k = 0; k < CF::MAXC; ++k)
-    if (dsts[k] >= 0) *reinterpret_cast<u32x4*>(lds + dsts[k]) = vals[k];
-  if (tid < T) s.bs[tid] = bval;
-  if constexpr (QUEUE) {
-    // the ticket was issued before the staged loads just waited for, so it has landed
-    if (tid == 0) s.next[slot] = ticket;
-  }
-  __syncthreads();  // B0: staged inputs visible; this WG's conv-cache reads have landed
-
-  // q/k conv-cache ownership: count this WG in now (its reads have landed); the count
-  // is read only after the prologue math, so nothing waits on the atomic until then.
-  uint32_t prev = 0;
-  if (!CF::PRE && tid == 0 && a.group > 1)
-    prev = __hip_atomic_fetch_add(a.counters + (size_t)n * H + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
   // ---------------- phase 1a: conv + SiLU, one task per pair of staged channels, sliding
   // over the tokens (taps and the three cached inputs read once per channel); the raw
   // window each token leaves behind, e[t+1..t+3], is staged in LDS in the layout of its
   // output row, two channels (six values) per write
   // q/k windows are written out by one WG of the group (all tokens) and the rolled q/k
   // cache by the last WG to count in (the last token's window): a WG stages only those
-  const bool qk_owner = (hv % a.g == 0) && vt == 0;
   for (int pr = tid; pr < NCH / 2; pr += NTHR) {
     const int ch = 2 * pr;  // the pair never straddles the q | k | v blocks (all even)
     const int t_stage = ch < 2 * K && !qk_owner ? T - 1 : 0;  // first token whose window is staged
@@ -565,11 +462,19 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
       }
       s.row[row_slot<CF>(t, i)].z = exp_fast(ld);
     }
-    if (tid < T) s.betas[tid] = sigmoid_fast(up(s.bs[tid]));
+    if (tid < T) s.betas[tid] = sigmoid_fast(up((R)s.bs[tid]));
   }
 
-  __syncthreads();  // B1
+}
 
+// Phase 2a of a unit: q/k l2norm per token (one wave per token), decay folded in.
+template <class CF, typename R>
+__device__ __forceinline__ void l2norm_tokens(const Args& a, Smem<CF, R>& s) {
+  constexpr int K = CF::K;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int T = a.T;
+  __builtin_assume(T >= 1 && T <= CF::TMAX);
   // ---------------- phase 2a: q/k l2norm per token (one wave per token), fold alpha in
   for (int t = wave; t < T; t += CF::NWT) {
     float kx[2], qx[2];
@@ -605,14 +510,15 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
     if (lane == 0) s.qk[t] = sqk * rk * rq;
   }
 
-  if (tid == 0) {
-    const bool last = a.group <= 1 || prev == (uint32_t)(a.group - 1);
-    if (last && a.group > 1)
-      __hip_atomic_store(a.counters + (size_t)n * H + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s.last = last;
-  }
-  __syncthreads();  // B2
+}
 
+template <class CF, typename R>
+__device__ __forceinline__ void grid_raw_copies(const Args& a, Smem<CF, R>& s, const UnitAt& u, const bool qk_owner) {
+  constexpr int K = CF::K, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
+  const int tid = threadIdx.x;
+  const int T = a.T, H = a.H, C = a.C;
+  const int h = u.h, hv = u.hv, vt = u.vt, cs_row = u.cs_row, in_row = u.in_row;
+  R* cstate = static_cast<R*>(a.conv_state);
   // ---------------- grid schedule: every raw copy of the unit before the first token's
   // sums (the conv window of each token, then the rolled conv cache, with the same owners
   // as the queue's per-token copies in the token loop). A grid WG runs one unit and exits;
@@ -623,7 +529,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   // token loop waits on none of them. Issued here on the queue schedule they cost 1-3 %
   // (measured): there the copies of a unit overlap the next unit's loads anyway, and here
   // they delay its first snapshot.
-  if constexpr (!CF::PRE && !QUEUE) {
+  if constexpr (!CF::PRE) {
     constexpr int VQK = 3 * K / E16;
     constexpr int VV = 3 * CF::WT / E16;
     constexpr int MAXR = CF::TMAX * (2 * VQK + VV) + VV + 2 * VQK;
@@ -673,6 +579,26 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
     }
   }
 
+}
+
+// The token loop of a unit: the gated delta-rule update of the state tile S held in
+// registers, o, the snapshot of every token, and (queue schedules) each token's raw copies.
+template <class CF, typename R, bool QUEUE>
+__device__ __forceinline__ void token_loop(const Args& a, Smem<CF, R>& s, f32x4 (&S)[CF::RPL], const UnitAt& u,
+                                           const bool qk_owner) {
+  constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
+  constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int T = a.T, H = a.H, HV = a.HV, C = a.C;
+  __builtin_assume(T >= 1 && T <= CF::TMAX);
+  const int n = u.n, hv = u.hv, h = u.h, vt = u.vt, cs_row = u.cs_row, in_row = u.in_row;
+  R* cstate = static_cast<R*>(a.conv_state);
+  const int grp = wave / CF::NW, wv = wave - grp * CF::NW;
+  const int c4 = lane % LPR, qq = lane / LPR;
+  const int col = vt * CF::WT + grp * VT + c4 * 4;
+  const int row0 = wv * CF::RW + qq;
+  const size_t KV = (size_t)K * V;
   // ---------------- token loop
   float* snap = a.inter_ssm + (size_t)row0 * V + col;
   for (int t = 0; t < T; ++t) {
@@ -805,6 +731,140 @@ __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const
   }
 }
 
+// One (sequence, value head, V-tile) unit of the step, by the whole workgroup. Under the
+// queue schedule (QUEUE) thread 0 also takes a ticket for the workgroup's next unit as
+// the unit starts and leaves it in s.next[slot] before the first barrier.
+template <class CF, typename R, bool QUEUE>
+__device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const int lb, const int slot) {
+  constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
+  constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
+
+  const int tid = threadIdx.x;
+  // The ticket is drawn by thread 0 and read only by thread 0, on the same path, so no
+  // other lane ever reads it. It gets no initial value on purpose: one would make the
+  // compiler set the register at the top of every unit, and that write waits first for
+  // every store of the previous unit still in flight (measured; a zero, an empty asm
+  // defining it and __builtin_nondeterministic_value all do).
+  uint32_t ticket;
+  if constexpr (QUEUE)
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(a.counters + (size_t)a.N * a.H, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int wave = tid >> 6, lane = tid & 63;
+  const int T = a.T, H = a.H, HV = a.HV, C = a.C;
+  __builtin_assume(T >= 1 && T <= CF::TMAX);
+  const int vt = lb % CF::NVT;
+  const int unit = lb / CF::NVT;  // n * HV + hv
+  const int hv = unit % HV, n = unit / HV;
+  const int h = hv / a.g;
+  // pool rows of this sequence: conv cache, state, and the snapshot / window pools
+  const int cs_row = a.cs_idx ? a.cs_idx[n] : n;
+  const int st_row = a.st_idx ? a.st_idx[n] : n;
+  const int in_row = a.in_idx ? a.in_idx[n] : n;
+  if (cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots || in_row < 0 ||
+      in_row >= a.in_slots) {
+    // padding entry: the whole unit (and its group) skips, nothing is read or written
+    if constexpr (QUEUE)
+      if (tid == 0) s.next[slot] = ticket;
+    return;
+  }
+
+  const typename CF::XR* __restrict__ xq = static_cast<const typename CF::XR*>(a.mixed_qkv);
+  const R* __restrict__ wq = static_cast<const R*>(a.conv_weight);
+  R* cstate = static_cast<R*>(a.conv_state);
+  const R* __restrict__ gq = static_cast<const R*>(a.gate);
+  const R* __restrict__ bq = static_cast<const R*>(a.beta);
+
+  // ---------------- prologue: issue every 16-byte load of the WG's small inputs
+  const int PA = NCH / CF::XE16;
+  const int nA = T * PA;              // new tokens
+  const int nB = CF::PRE ? 0 : 3 * NCH / E16;  // conv cache
+  const int nC = CF::PRE ? 0 : 4 * NCH / E16;  // conv taps
+  const int nD = T * K / E16;         // gate
+  const int nE = K / 4;               // dt_bias (fp32)
+  const int total = nA + nB + nC + nD + nE;
+  u32x4 vals[CF::MAXC];
+  int dsts[CF::MAXC];
+  char* lds = reinterpret_cast<char*>(&s);
+  const float alog = a.A_log[hv];
+  // Every slot loads unconditionally (a slot past the end re-reads the last vector and
+  // is not stored), so the loads issue back to back with no wait between them.
+#pragma unroll
+  for (int k = 0; k < CF::MAXC; ++k) {
+    const int cv = tid + k * NTHR;
+    int ci = cv < total ? cv : total - 1;
+    const void* src;
+    int dst;
+    if (ci < nA) {
+      const int t = ci / PA, pe = (ci - t * PA) * CF::XE16;
+      src = xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt);
+      dst = (int)((char*)&s.xs[t * NCH + pe] - lds);
+    } else if ((ci -= nA) < nB) {
+      const int e = ci * E16, lc = e / 3;
+      src = cstate + ((size_t)cs_row * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3);
+      dst = (int)((char*)&s.cs[e] - lds);
+    } else if ((ci -= nB) < nC) {
+      const int e = ci * E16, lc = e / 4;
+      src = wq + (size_t)gchan<CF>(lc, h, H, hv, vt) * 4 + (e - lc * 4);
+      dst = (int)((char*)&s.ws[e] - lds);
+    } else if ((ci -= nC) < nD) {
+      const int e = ci * E16, t = e / K;
+      src = gq + ((size_t)(n * T + t) * HV + hv) * K + (e - t * K);
+      dst = (int)((char*)&s.gs[e] - lds);
+    } else {
+      ci -= nD;
+      src = a.dt_bias + (size_t)hv * K + ci * 4;
+      dst = (int)((char*)&s.dtb[ci * 4] - lds);
+    }
+    vals[k] = *reinterpret_cast<const u32x4*>(src);
+    dsts[k] = cv < total ? dst : -1;
+  }
+  const R bval = bq[(size_t)(n * T + (tid < T ? tid : T - 1)) * HV + hv];
+
+  // ---------------- state tile: 16-byte loads, left in flight through the prologue math
+  const int grp = wave / CF::NW, wv = wave - grp * CF::NW;  // column group, wave in the group
+  const int c4 = lane % LPR, qq = lane / LPR;
+  const int col = vt * CF::WT + grp * VT + c4 * 4;
+  const int row0 = wv * CF::RW + qq;  // this lane's rows: row0 + Q * r
+  const size_t KV = (size_t)K * V;
+  const float* sp = a.state + ((size_t)st_row * HV + hv) * KV + (size_t)row0 * V + col;
+  f32x4 S[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r)
+    S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)r * Q * V));
+
+#pragma unroll
+  for (int k = 0; k < CF::MAXC; ++k)
+    if (dsts[k] >= 0) *reinterpret_cast<u32x4*>(lds + dsts[k]) = vals[k];
+  if (tid < T) s.bs[tid] = (uint32_t)bval;
+  if constexpr (QUEUE) {
+    // the ticket was issued before the staged loads just waited for, so it has landed
+    if (tid == 0) s.next[slot] = ticket;
+  }
+  __syncthreads();  // B0: staged inputs visible; this WG's conv-cache reads have landed
+
+  // q/k conv-cache ownership: count this WG in now (its reads have landed); the count
+  // is read only after the prologue math, so nothing waits on the atomic until then.
+  uint32_t prev = 0;
+  if (!CF::PRE && tid == 0 && a.group > 1)
+    prev = __hip_atomic_fetch_add(a.counters + (size_t)n * H + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  const bool qk_owner = (hv % a.g == 0) && vt == 0;
+  conv_and_gates<CF, R>(a, s, qk_owner, alog);
+  __syncthreads();  // B1
+  l2norm_tokens<CF, R>(a, s);
+  if (tid == 0) {
+    const bool last = a.group <= 1 || prev == (uint32_t)(a.group - 1);
+    if (last && a.group > 1)
+      __hip_atomic_store(a.counters + (size_t)n * H + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.last = last;
+  }
+  __syncthreads();  // B2
+
+  const UnitAt u{n, hv, h, vt, cs_row, in_row};
+  if constexpr (!QUEUE) grid_raw_copies<CF, R>(a, s, u, qk_owner);
+  token_loop<CF, R, QUEUE>(a, s, S, u, qk_owner);
+}
+
 // Grid schedule: one workgroup per unit; the hardware starts each workgroup as a slot on
 // a CU frees up, and hands workgroups to the XCDs round-robin, so every XCD gets the same
 // number of units whatever its speed.
@@ -840,6 +900,299 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_queue_kernel(const Args a
       __hip_atomic_store(q + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// Stream schedule: the queue schedule with the loads taken off the compute waves. A fifth
+// wave, the producer, pulls the units from the counter and loads each one's inputs and
+// state tile straight into LDS (LDS-direct loads) while the four compute waves run the
+// unit before it. The compute waves then issue no vector-memory read at all; on CDNA the
+// vector-memory counter of a wave completes in issue order, so a load of theirs would wait
+// for every snapshot store they issued before it, and this is what made a queue unit's
+// staged phase longer than a grid unit's. The producer's counter holds only its own loads
+// and atomics, and it waits on them only before the barrier that hands the next unit over,
+// with the whole token loop of the current unit as slack.
+//
+// When the producer issues the next unit's state tile:
+//   kPrefetchAfterConv:  with its other inputs, once the compute waves finished the conv and
+//                        gates of the current unit (LDS staging free);
+//   kPrefetchAtStart:    as soon as the compute waves hold the current unit's state in
+//                        registers (one more barrier), so that the state read overlaps the
+//                        conv phase as well. Measured faster up to 4 GiB of snapshots per call
+//                        at T >= 3 and slower beyond (the dispatch rule below).
+// Loading it any later, in front of a token's snapshot stores, measured 4-20 % slower.
+enum StatePrefetch { kPrefetchAfterConv = 1, kPrefetchAtStart = 2 };
+
+// A unit as the producer hands it over: its index (lb < 0: no more units), pool rows,
+// whether its rows are inside the pools (a padding unit is skipped whole), and whether it
+// was the last of its q/k group to count in.
+struct UnitDesc {
+  int lb, cs_row, st_row, in_row, last, valid;
+};
+
+template <class CF, typename R>
+struct alignas(16) StreamSmem {
+  Smem<CF, R> s;                // the staged inputs (written by the producer) and the unit's rows
+  f32x4 st[CF::K * CF::V / 4];  // the next unit's state tile, K rows of V floats as in HBM
+  float alog;                   // A_log of the next unit's value head
+  UnitDesc desc[2];             // the unit handed over at the last barrier, by parity
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void global_void_t;
+
+// LDS-direct load: every active lane reads BYTES at src, and the wave writes lane i's
+// value to lds + 16 i (16-byte loads) or lds + 4 i (4- and 2-byte loads, zero-extended).
+// The LDS address must be the same for every lane. NT: the streaming hint.
+template <int BYTES, bool NT = false>
+__device__ __forceinline__ void lds_direct(const void* src, void* lds) {
+  if constexpr (BYTES == 16 && NT)
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds, 16, 0, 2);
+  else if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds, 16, 0, 0);
+  else if constexpr (BYTES == 4)
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds, 4, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds, 2, 0, 0);
+}
+
+// The producer's side of the compute waves' barriers. A plain barrier, with no wait, so
+// that the producer's loads stay in flight across it; the memory clobber keeps the
+// compiler from moving the loads across it.
+__device__ __forceinline__ void producer_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The hand-over barrier: every load of the producer has landed in LDS and its unit
+// descriptor is written before the compute waves pass it.
+__device__ __forceinline__ void producer_handover() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Producer: the pool rows of unit lb (lb < 0: no unit).
+template <class CF>
+__device__ __forceinline__ UnitDesc stream_rows(const Args& a, const int lb) {
+  UnitDesc d;
+  d.lb = lb;
+  d.last = 1;
+  d.cs_row = d.st_row = d.in_row = 0;
+  d.valid = 0;
+  if (lb < 0) return d;
+  const int n = (lb / CF::NVT) / a.HV;
+  d.cs_row = a.cs_idx ? a.cs_idx[n] : n;
+  d.st_row = a.st_idx ? a.st_idx[n] : n;
+  d.in_row = a.in_idx ? a.in_idx[n] : n;
+  d.valid = !(d.cs_row < 0 || d.cs_row >= a.cs_slots || d.st_row < 0 || d.st_row >= a.st_slots || d.in_row < 0 ||
+              d.in_row >= a.in_slots);
+  return d;
+}
+
+// Producer: issue the LDS-direct loads of a valid unit's small inputs into the staging
+// record, each block of 16-byte vectors in the order the grid and queue units stage them
+// (the same LDS layout), 64 vectors per instruction. Not waited for here.
+template <class CF, typename R>
+__device__ __forceinline__ void stream_stage_inputs(const Args& a, StreamSmem<CF, R>& ss, const UnitDesc& d,
+                                                    const int lane) {
+  constexpr int K = CF::K, NCH = CF::NCH, E16 = CF::E16;
+  const int T = a.T, H = a.H, HV = a.HV, C = a.C;
+  const int vt = d.lb % CF::NVT;
+  const int unit = d.lb / CF::NVT;
+  const int hv = unit % HV, n = unit / HV;
+  const int h = hv / a.g;
+  Smem<CF, R>& s = ss.s;
+  const R* xq = static_cast<const R*>(a.mixed_qkv);
+  const R* wq = static_cast<const R*>(a.conv_weight);
+  const R* cq = static_cast<const R*>(a.conv_state);
+  const R* gq = static_cast<const R*>(a.gate);
+  const R* bq = static_cast<const R*>(a.beta);
+  const int PA = NCH / E16;
+  const int nA = T * PA;  // new tokens
+  for (int k = 0; k * 64 < nA; ++k) {
+    const int ci = k * 64 + lane;
+    if (ci < nA) {
+      const int t = ci / PA, pe = (ci - t * PA) * E16;
+      lds_direct<16>(xq + (size_t)(n * T + t) * C + gchan<CF>(pe, h, H, hv, vt),
+                     reinterpret_cast<char*>(s.xs) + k * 1024);
+    }
+  }
+  constexpr int nB = 3 * NCH / E16;  // conv cache
+#pragma unroll
+  for (int k = 0; k * 64 < nB; ++k) {
+    const int ci = k * 64 + lane;
+    if (ci < nB) {
+      const int e = ci * E16, lc = e / 3;
+      lds_direct<16>(cq + ((size_t)d.cs_row * C + gchan<CF>(lc, h, H, hv, vt)) * 3 + (e - lc * 3),
+                     reinterpret_cast<char*>(s.cs) + k * 1024);
+    }
+  }
+  constexpr int nC = 4 * NCH / E16;  // conv taps
+#pragma unroll
+  for (int k = 0; k * 64 < nC; ++k) {
+    const int ci = k * 64 + lane;
+    if (ci < nC) {
+      const int e = ci * E16, lc = e / 4;
+      lds_direct<16>(wq + (size_t)gchan<CF>(lc, h, H, hv, vt) * 4 + (e - lc * 4),
+                     reinterpret_cast<char*>(s.ws) + k * 1024);
+    }
+  }
+  const int nD = T * K / E16;  // gate
+  for (int k = 0; k * 64 < nD; ++k) {
+    const int ci = k * 64 + lane;
+    if (ci < nD) {
+      const int e = ci * E16, t = e / K;
+      lds_direct<16>(gq + ((size_t)(n * T + t) * HV + hv) * K + (e - t * K), reinterpret_cast<char*>(s.gs) + k * 1024);
+    }
+  }
+  constexpr int nE = K / 4;  // dt_bias (fp32)
+#pragma unroll
+  for (int k = 0; k * 64 < nE; ++k) {
+    const int ci = k * 64 + lane;
+    if (ci < nE) lds_direct<16>(a.dt_bias + (size_t)hv * K + ci * 4, reinterpret_cast<char*>(s.dtb) + k * 1024);
+  }
+  if (lane < T) lds_direct<(int)sizeof(R)>(bq + (size_t)(n * T + lane) * HV + hv, s.bs);
+  if (lane == 0) lds_direct<4>(a.A_log + hv, &ss.alog);
+}
+
+// Producer: issue the LDS-direct loads of a valid unit's state tile, 1 KiB per
+// instruction, with the streaming hint. Not waited for here.
+template <class CF, typename R>
+__device__ __forceinline__ void stream_stage_state(const Args& a, StreamSmem<CF, R>& ss, const UnitDesc& d,
+                                                   const int lane) {
+  constexpr int K = CF::K, V = CF::V;
+  const int hv = (d.lb / CF::NVT) % a.HV;
+  const float* sp = a.state + ((size_t)d.st_row * a.HV + hv) * ((size_t)K * V) + lane * 4;
+#pragma unroll
+  for (int j = 0; j < K * V / 256; ++j)
+    lds_direct<16, true>(sp + j * 256, reinterpret_cast<char*>(ss.st) + j * 1024);
+}
+
+// Producer: count unit d into its q/k group once its reads have landed (the caller has
+// waited for them), as a grid or queue unit counts itself in after its staged loads;
+// returns whether it was the last of the group, which then writes the rolled q/k cache.
+__device__ __forceinline__ int stream_count_in(const Args& a, const UnitDesc& d, const int nvt, const int lane) {
+  if (!d.valid || a.group <= 1) return 1;
+  const int unit = d.lb / nvt;
+  const int hv = unit % a.HV, n = unit / a.HV, h = hv / a.g;
+  uint32_t* c = a.counters + (size_t)n * a.H + h;
+  uint32_t prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
+  const int last = prev == (uint32_t)(a.group - 1);
+  if (last && lane == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// The producer wave. It passes exactly the barriers the compute waves pass for each unit
+// (B0 with kPrefetchAtStart, B1, B2, one per token, then the hand-over; a padding unit only
+// the hand-over), decided by the same descriptor and T.
+template <class CF, typename R>
+__device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>& ss, const int units, const int G) {
+  const int lane = threadIdx.x & 63;
+  uint32_t* qc = a.counters + (size_t)a.N * a.H;  // ticket, then leave count
+  UnitDesc d = stream_rows<CF>(a, xcd_order(blockIdx.x, G));
+  if (d.valid) {
+    stream_stage_inputs<CF, R>(a, ss, d, lane);
+    stream_stage_state<CF, R>(a, ss, d, lane);
+  }
+  uint32_t tk = 0;
+  if (lane == 0) tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  tk = (uint32_t)__builtin_amdgcn_readfirstlane((int)tk);
+  d.last = stream_count_in(a, d, CF::NVT, lane);
+  if (lane == 0) ss.desc[0] = d;
+  UnitDesc nd = stream_rows<CF>(a, kda_queue_unit(tk, units, G));  // the unit after it
+  producer_handover();
+  for (int it = 0;; ++it) {
+    const UnitDesc cur = ss.desc[it & 1];
+    if (cur.lb < 0) break;
+    const bool drew = nd.lb >= 0;
+    const bool state_at_start = a.prefetch == kPrefetchAtStart && cur.valid;
+    if (state_at_start) {
+      producer_barrier();  // B0: the compute waves hold the state tile in registers
+      if (nd.valid) stream_stage_state<CF, R>(a, ss, nd, lane);
+    }
+    if (cur.valid) producer_barrier();  // B1: the compute waves are done with the staged inputs
+    if (drew) {
+      if (nd.valid) {
+        stream_stage_inputs<CF, R>(a, ss, nd, lane);
+        if (!state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane);
+      }
+      if (lane == 0) tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (cur.valid) {
+      producer_barrier();  // B2
+      for (int t = 0; t < a.T; ++t) producer_barrier();  // one per token
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (drew) {
+      tk = (uint32_t)__builtin_amdgcn_readfirstlane((int)tk);
+      nd.last = stream_count_in(a, nd, CF::NVT, lane);
+    }
+    if (lane == 0) ss.desc[(it + 1) & 1] = nd;
+    nd = stream_rows<CF>(a, drew ? kda_queue_unit(tk, units, G) : -1);
+    producer_handover();
+  }
+  // every ticket this workgroup drew has been seen (the last one past the end): count out;
+  // the last workgroup to leave zeroes the ticket and leave counts for the next call
+  if (lane == 0) {
+    const uint32_t left = __hip_atomic_fetch_add(qc + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == (uint32_t)G - 1) {
+      __hip_atomic_store(qc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(qc + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// The compute waves' part of one unit the producer staged: the same phases and barriers
+// as a queue unit, from LDS.
+template <class CF, typename R>
+__device__ __forceinline__ void stream_unit(const Args& a, StreamSmem<CF, R>& ss, const UnitDesc& d) {
+  constexpr int V = CF::V, RPL = CF::RPL, Q = CF::Q, LPR = CF::LPR;
+  Smem<CF, R>& s = ss.s;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int vt = d.lb % CF::NVT;
+  const int unit = d.lb / CF::NVT;
+  const int hv = unit % a.HV, n = unit / a.HV;
+  const int h = hv / a.g;
+  const int grp = wave / CF::NW, wv = wave - grp * CF::NW;
+  const int c4 = lane % LPR, qq = lane / LPR;
+  const int col = vt * CF::WT + grp * CF::VT + c4 * 4;
+  const int row0 = wv * CF::RW + qq;
+  f32x4 S[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) S[r] = ss.st[((row0 + r * Q) * V + col) / 4];
+  const float alog = ss.alog;
+  if (a.prefetch == kPrefetchAtStart) __syncthreads();  // B0: the producer may load the next state tile
+  const bool qk_owner = (hv % a.g == 0) && vt == 0;
+  conv_and_gates<CF, R>(a, s, qk_owner, alog);
+  __syncthreads();  // B1
+  l2norm_tokens<CF, R>(a, s);
+  if (tid == 0) s.last = d.last;
+  __syncthreads();  // B2
+  token_loop<CF, R, true>(a, s, S, UnitAt{n, hv, h, vt, d.cs_row, d.in_row}, qk_owner);
+}
+
+// Whole-V workgroups of CF::NTHR compute threads plus the producer wave, one per CU (the
+// LDS record alone holds a CU), grid = resident workgroups (<= units).
+template <class CF, typename R>
+__global__ __launch_bounds__(CF::NTHR + 64) void kda_verify_stream_kernel(const Args a) {
+  __shared__ StreamSmem<CF, R> ss;
+  const int units = a.N * a.HV * CF::NVT;
+  const int G = gridDim.x;
+  if ((int)threadIdx.x >= CF::NTHR) {
+    stream_producer<CF, R>(a, ss, units, G);
+    return;
+  }
+  __syncthreads();  // the first unit is in LDS
+  for (int it = 0;; ++it) {
+    const UnitDesc d = ss.desc[it & 1];
+    if (d.lb < 0) break;
+    if (d.valid) stream_unit<CF, R>(a, ss, d);
+    __syncthreads();  // hand-over: the producer has staged the next unit
+  }
+}
+
+// Whether the stream schedule's LDS record of CF fits a CU (160 KiB).
+template <class CF, typename R>
+constexpr bool stream_fits() {
+  return CF::K == 128 && CF::WT == CF::V && CF::G == 1 && !CF::PRE && sizeof(StreamSmem<CF, R>) <= 160 * 1024;
 }
 
 // Unfused form, first kernel: width-4 causal conv + SiLU for every channel, one thread per
@@ -963,8 +1316,10 @@ struct Tile {
   int stp;             // StorePolicy
   int occ = 0;         // workgroups per CU cap (lds_reservation), 0 = none
   int g = 1;           // column groups of 4 waves sharing the WG's staging and conv
-  bool queue = false;  // resident workgroups pulling units from a counter (whole-V only)
+  bool queue = false;   // resident workgroups pulling units from a counter (whole-V only)
   int order = kOrderXcdRanges;  // UnitOrder of the grid
+  bool stream = false;  // the queue with a producer wave (whole-V, one group, T <= 8)
+  int prefetch = kPrefetchAfterConv;  // StatePrefetch of the stream schedule
 };
 using LaunchFn = hipError_t (*)(const Args&, const Tile&, hipStream_t);
 
@@ -1010,9 +1365,21 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
   Args copy = a;
   copy.group = a.g * CF::NVT;
   copy.order = tl.order;
+  copy.prefetch = tl.prefetch;
   void* args[] = {&copy};
   const size_t want = lds_reservation(tl.occ), have = sizeof(Smem<CF, R>);
   const size_t dyn = want > have ? want - have : 0;
+  if (tl.stream) {
+    if constexpr (stream_fits<CF, R>()) {
+      const void* fn = reinterpret_cast<const void*>(&kda_verify_stream_kernel<CF, R>);
+      const long long slots = resident_workgroups(fn, CF::NTHR + 64, 0, 1);
+      if (slots <= 0) return hipErrorInvalidConfiguration;
+      return hipLaunchKernel(fn, dim3((unsigned)(units < slots ? units : slots)), dim3(CF::NTHR + 64), args, 0,
+                             stream);
+    } else {
+      return hipErrorInvalidConfiguration;  // whole-V, one group, T <= 8 only (check_params)
+    }
+  }
   if (tl.queue) {
     if constexpr (CF::WT == CF::V && !CF::PRE) {
       const void* fn = reinterpret_cast<const void*>(&kda_verify_queue_kernel<CF, R>);
@@ -1040,7 +1407,13 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 //      (policy 1) at T = 2 and 4 and with four groups, device scope (policy 2) otherwise;
 //   3. T = 1, or < 1024 units, or < 2048 units at T = 2: the uncapped whole-V grid;
 //   4. < 2048 units at T = 3, 4: two whole-V workgroups per CU;
-//   5. otherwise the queue, one whole-V workgroup per CU, two column groups at T = 2.
+//   5. otherwise the stream schedule (up to T = 8; the queue with two column groups at
+//      T = 2 and one beyond, above T = 8): the next unit's state loaded at the start of
+//      the current one at T >= 3 up to 65536 snapshot tiles of 64 KiB (4 GiB) per call,
+//      after its conv otherwise. Measured against the queue on 40 shapes of 1024-32768
+//      units, T = 2-8: +2-5 % up to 16384 units at T = 3-6 (large_batch +3.7 %, gva +3.5 %),
+//      +0.3-3 % on the larger calls with the later load, 1-2 % behind on two T = 8 shapes
+//      with shared q/k heads at 8192 units; below 2048 units it trails the grid buckets.
 // Buckets 3-5 store at device scope. The unit order follows from the launch (choose_tile):
 // pairs for uncapped whole-V grids. Every launch uses the same K split (32 rows per wave)
 // and partial-sum tree, so all return bit-identical results; cap, schedule and order only
@@ -1059,7 +1432,11 @@ Tile auto_tile_128(long long units, int T) {
   }
   if (T == 1 || units < 1024 || (units < 2048 && T == 2)) return Tile{128, kStoreNTDev};
   if (units < 2048 && T <= 4) return Tile{128, kStoreNTDev, 2};
-  return Tile{128, kStoreNTDev, 1, T == 2 ? 2 : 1, true};
+  if (T > 8) return Tile{128, kStoreNTDev, 1, 1, true};
+  Tile t{128, kStoreNTDev, 1, 1};
+  t.stream = true;
+  t.prefetch = T >= 3 && units * T <= 65536 ? kPrefetchAtStart : kPrefetchAfterConv;
+  return t;
 }
 
 // The AUTO choice with the caller's overrides applied. A cap belongs to the AUTO tile: when
@@ -1075,6 +1452,7 @@ Tile choose_tile(const kda_verify_params* p) {
       t.occ = 0;
       t.g = 1;
       t.queue = false;
+      t.stream = false;
     }
     if (p->tile_columns != 0)
       t.vt = p->tile_columns;
@@ -1082,8 +1460,8 @@ Tile choose_tile(const kda_verify_params* p) {
       t.vt = 128;
     else if (p->variant == KDA_VARIANT_SMALL)
       t.vt = 32;
-    else if (p->schedule == 2 || p->column_groups > 1)
-      t.vt = 128;  // the queue and column groups run whole-V workgroups
+    else if (p->schedule >= 2 || p->column_groups > 1)
+      t.vt = 128;  // the queue, the stream and column groups run whole-V workgroups
     if (p->store_policy != 0) t.stp = p->store_policy == 2 ? kStoreNTDev : kStoreNT;
     // fp32 inputs at T > 8: a whole-V workgroup's staged inputs and conv windows would not
     // fit in LDS; two 64-column workgroups give the same bits
@@ -1091,13 +1469,28 @@ Tile choose_tile(const kda_verify_params* p) {
       t.vt = 64;
       t.g = 1;
       t.queue = false;
+      t.stream = false;
     }
   } else {
     t = K == 64 && V == 64 ? Tile{p->variant == KDA_VARIANT_SMALL ? 32 : 64, kStoreNT} : Tile{16, kStoreNT};
   }
   if (p->max_wg_per_cu != 0) t.occ = p->max_wg_per_cu == 8 ? 0 : p->max_wg_per_cu;
   if (p->column_groups != 0) t.g = p->column_groups;
-  if (p->schedule != 0) t.queue = p->schedule == 2;
+  if (p->schedule != 0) {
+    t.queue = p->schedule == 2;
+    t.stream = p->schedule == 3;
+  }
+  // the stream runs one whole-V group per CU: a caller's column groups or cap take the AUTO
+  // stream back to the queue, which honours them
+  if (t.stream && p->schedule != 3 && (t.g > 1 || t.occ != 1)) {
+    t.stream = false;
+    t.queue = true;
+  }
+  if (t.stream) {  // one whole-V workgroup (one group) per CU, held there by its LDS
+    t.g = 1;
+    t.occ = 1;
+    if (p->prefetch != 0) t.prefetch = p->prefetch;
+  }
   // unit order of the grid: pairs when whole-V workgroups run without a cap (every
   // workgroup resident at once), XCD ranges otherwise
   if (p->unit_order != 0)
@@ -1229,6 +1622,7 @@ void kda_verify_params_init(kda_verify_params* p, int32_t N, int32_t T, int32_t 
   p->column_groups = 0;
   p->schedule = 0;
   p->unit_order = 0;
+  p->prefetch = 0;
 }
 
 static kda_status check_params(const kda_verify_params* p) {
@@ -1262,8 +1656,15 @@ static kda_status check_params(const kda_verify_params* p) {
                     (p->tile_columns == 32 || p->tile_columns == 64 || p->tile_columns == 128);
     if (!ok) return KDA_ERR_UNSUPPORTED;
   }
-  if (p->schedule < 0 || p->schedule > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->schedule < 0 || p->schedule > 3) return KDA_ERR_UNSUPPORTED;
   if (p->unit_order < 0 || p->unit_order > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->prefetch < 0 || p->prefetch > 2) return KDA_ERR_UNSUPPORTED;
+  if (p->schedule == 3) {
+    // the stream: whole-V workgroups of one column group, one per CU, K = V = 128, T <= 8
+    const int wt = p->tile_columns != 0 ? p->tile_columns : p->variant == KDA_VARIANT_SMALL ? 32 : 128;
+    if (p->K != 128 || p->V != 128 || wt != 128 || p->T > 8 || p->column_groups > 1 || p->max_wg_per_cu > 1)
+      return KDA_ERR_UNSUPPORTED;
+  }
   if (p->schedule == 2) {
     // the queue runs whole-V workgroups
     bool ok = true;
@@ -1295,7 +1696,7 @@ int32_t kda_select_variant(const kda_verify_params* p) {
 
 kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, int32_t* store_policy,
                              int32_t* max_wg_per_cu, int32_t* column_groups, int32_t* schedule,
-                             int32_t* unit_order) {
+                             int32_t* unit_order, int32_t* prefetch) {
   const kda_status st = check_params(p);
   if (st != KDA_OK) return st;
   const Tile t = choose_tile(p);
@@ -1303,8 +1704,9 @@ kda_status kda_select_launch(const kda_verify_params* p, int32_t* tile_columns, 
   if (store_policy) *store_policy = t.stp == kStoreNTDev ? 2 : 1;
   if (max_wg_per_cu) *max_wg_per_cu = t.occ;
   if (column_groups) *column_groups = t.g;
-  if (schedule) *schedule = t.queue ? 2 : 1;
+  if (schedule) *schedule = t.stream ? 3 : t.queue ? 2 : 1;
   if (unit_order) *unit_order = t.order;
+  if (prefetch) *prefetch = t.stream ? t.prefetch : 0;
   return KDA_OK;
 }
 
@@ -1436,7 +1838,7 @@ kda_status launch_verify(const kda_verify_params* p, const PoolView& pv, const v
                          const float* dt_bias, const void* beta, const float* state, void* o, float* inter_ssm,
                          void* conv_window, void* workspace, hipStream_t stream, bool pre) {
   Tile tl = choose_tile(p);
-  if (pre) tl.queue = false;  // the unfused form keeps one workgroup per unit
+  if (pre) tl.queue = tl.stream = false;  // the unfused form keeps one workgroup per unit
   LaunchFn fn = pick_launch(p, tl, pre);
   if (!fn) return KDA_ERR_UNSUPPORTED;
   Args a;
@@ -1489,7 +1891,7 @@ kda_status kda_conv_verify_decode_unfused(const kda_verify_params* p, const kda_
   kda_status st = validate_verify(p, pools, &pv, mixed_qkv, conv_weight, conv_state, gate, A_log, dt_bias, beta,
                                   state, o, inter_ssm, conv_window, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
-  if (p->schedule == 2) return KDA_ERR_UNSUPPORTED;
+  if (p->schedule >= 2) return KDA_ERR_UNSUPPORTED;
   if (p->N == 0) return KDA_OK;
   if (!act) return KDA_ERR_NULL;
   if (misaligned(act)) return KDA_ERR_ALIGN;

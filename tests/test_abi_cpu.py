@@ -251,7 +251,10 @@ def test_tuning_overrides(lib):
     for bad in (dict(tile_columns=48), dict(store_policy=3), dict(max_wg_per_cu=3), dict(max_wg_per_cu=7),
                 dict(max_wg_per_cu=-1), dict(column_groups=3), dict(column_groups=8),
                 dict(tile_columns=64, column_groups=2), dict(variant=kda.VARIANT_SMALL, column_groups=4),
-                dict(dtype="f32", T=12, column_groups=2), dict(schedule=3), dict(schedule=-1),
+                dict(dtype="f32", T=12, column_groups=2), dict(schedule=4), dict(schedule=-1),
+                dict(schedule=3, T=9), dict(schedule=3, column_groups=2), dict(schedule=3, max_wg_per_cu=2),
+                dict(schedule=3, tile_columns=64), dict(schedule=3, variant=kda.VARIANT_SMALL),
+                dict(prefetch=3), dict(prefetch=-1),
                 dict(tile_columns=64, schedule=2), dict(variant=kda.VARIANT_SMALL, schedule=2),
                 dict(dtype="f32", T=12, schedule=2), dict(unit_order=3), dict(unit_order=-1)):
         kw = dict(bad)
@@ -286,12 +289,12 @@ def test_every_accepted_override_names_a_built_launch(lib):
     p = kda.make_params(1, 4, 8, 8, 128, 128)
     assert kda.select_launch(p)["tile_columns"] == 32
     p = kda.make_params(1, 4, 8, 8, 128, 128, column_groups=2)
-    assert tuple(kda.select_launch(p).values()) == (128, 1, 0, 2, 1, 2)
+    assert tuple(kda.select_launch(p).values()) == (128, 1, 0, 2, 1, 2, 0)
     for N, T, H, HV, dt in ((64, 2, 16, 32, "bf16"), (1, 4, 8, 8, "bf16"), (512, 8, 16, 64, "bf16"),
                             (8, 12, 2, 2, "f32"), (32, 1, 16, 16, "bf16"), (128, 3, 16, 32, "bf16")):
         for tile in (0, 32, 64, 128):
             for groups in (0, 1, 2, 4):
-                for sched in (0, 1, 2):
+                for sched in (0, 1, 2, 3):
                     for variant in (kda.VARIANT_AUTO, kda.VARIANT_SMALL, kda.VARIANT_LARGE):
                         p = kda.make_params(N, T, H, HV, 128, 128, dtype=dt, tile_columns=tile, column_groups=groups,
                                             schedule=sched, variant=variant)
@@ -303,8 +306,11 @@ def test_every_accepted_override_names_a_built_launch(lib):
                         assert key in BUILT_128, (N, T, H, HV, dt, tile, groups, sched, variant, got)
                         if dt == "f32" and T > 8:
                             assert got["tile_columns"] < 128
-                        if got["schedule"] == 2:
+                        if got["schedule"] >= 2:
                             assert got["tile_columns"] == 128
+                        if got["schedule"] == 3:  # the stream kernel: one group, T <= 8
+                            assert got["column_groups"] == 1 and T <= 8 and got["max_wg_per_cu"] == 1
+                            assert got["prefetch"] in (1, 2)
 
 
 def test_prepared_call_checks_arguments_once():
@@ -323,14 +329,14 @@ def test_prepared_call_checks_arguments_once():
 
 def test_select_launch_follows_the_dispatch_rule(lib):
     """The AUTO rule (tile, stores, workgroups-per-CU cap, column groups, schedule: 1 grid,
-    2 queue) on the named workloads and at the edges of its five buckets, and the overrides
-    winning over it."""
+    2 queue, 3 stream) on the named workloads and at the edges of its five buckets, and the
+    overrides winning over it."""
     L = lambda *shape, **kw: tuple(kda.select_launch(kda.make_params(*shape, **kw)).values())[:5]
     assert L(2, 2, 2, 2, 16, 16) == (16, 1, 0, 1, 1)            # tiny: the only K = V = 16 tile
     assert L(32, 4, 16, 16, 128, 128) == (128, 1, 0, 1, 1)       # small batch: 512 units, T = 4
-    assert L(64, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 2)       # GVA: 2048 units, T = 3
-    assert L(256, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 2)      # large batch: 8192 units
-    assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 2)      # max bandwidth: 32768 units, T = 8
+    assert L(64, 3, 16, 32, 128, 128) == (128, 2, 1, 1, 3)       # GVA: 2048 units, T = 3
+    assert L(256, 4, 32, 32, 128, 128) == (128, 2, 1, 1, 3)      # large batch: 8192 units
+    assert L(512, 8, 16, 64, 128, 128) == (128, 2, 1, 1, 3)      # max bandwidth: 32768 units, T = 8
     # 1. <= 64 units, and <= 128 at T = 2: the 32-column split
     assert L(1, 4, 8, 8, 128, 128) == (32, 1, 0, 1, 1)
     assert L(4, 4, 16, 16, 128, 128) == (32, 1, 0, 1, 1)
@@ -358,13 +364,25 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     # 4. two per CU below 2048 units at T = 3, 4
     assert L(32, 3, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
     assert L(63, 4, 16, 32, 128, 128) == (128, 2, 2, 1, 1)
-    # 5. the queue, one per CU: from 2048 units at T = 2-4, from 1024 at T >= 5
-    assert L(64, 2, 16, 32, 128, 128) == (128, 2, 1, 2, 2)
-    assert L(64, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
-    assert L(32, 5, 16, 32, 128, 128) == (128, 2, 1, 1, 2)
+    # 5. the stream, one per CU: from 2048 units at T = 2-4, from 1024 at T >= 5; the
+    # queue above T = 8
+    assert L(64, 2, 16, 32, 128, 128) == (128, 2, 1, 1, 3)
+    assert L(64, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 3)
+    assert L(32, 5, 16, 32, 128, 128) == (128, 2, 1, 1, 3)
     assert L(31, 8, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
-    assert L(32, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(32, 8, 32, 32, 128, 128) == (128, 2, 1, 1, 3)
     assert L(1024, 16, 8, 8, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(128, 9, 8, 16, 128, 128) == (128, 2, 1, 1, 2)
+    assert L(64, 8, 16, 32, 128, 128, dtype="f32") == (128, 2, 1, 1, 3)
+    # the stream's state prefetch: at the start at T >= 3 up to 65536 snapshot tiles per call,
+    # after the conv otherwise; the override wins
+    F = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["prefetch"]
+    assert F(64, 3, 16, 32, 128, 128) == 2 and F(256, 4, 32, 32, 128, 128) == 2
+    assert F(256, 8, 32, 32, 128, 128) == 2                      # 65536 tiles
+    assert F(512, 8, 16, 64, 128, 128) == 1 and F(512, 4, 16, 64, 128, 128) == 1
+    assert F(256, 2, 32, 32, 128, 128) == 1                      # T = 2
+    assert F(256, 4, 32, 32, 128, 128, prefetch=1) == 1 and F(512, 8, 16, 64, 128, 128, prefetch=2) == 2
+    assert F(32, 4, 16, 16, 128, 128) == 0 and F(1024, 16, 8, 8, 128, 128) == 0  # not the stream
     # overrides
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32, store_policy=2, max_wg_per_cu=6) == (32, 2, 6, 1, 1)
     assert L(256, 4, 32, 32, 128, 128, tile_columns=32) == (32, 2, 0, 1, 1)   # the AUTO cap goes with its tile
@@ -377,7 +395,15 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(32, 4, 32, 32, 128, 128, column_groups=4) == (128, 2, 2, 4, 1)
     assert L(3, 16, 1, 4, 64, 64, max_wg_per_cu=2) == (64, 1, 2, 1, 1)
     assert L(256, 4, 32, 32, 128, 128, schedule=1) == (128, 2, 1, 1, 1)      # the grid, AUTO cap kept
+    assert L(256, 4, 32, 32, 128, 128, schedule=2) == (128, 2, 1, 1, 2)      # the queue, AUTO cap kept
     assert L(32, 4, 32, 32, 128, 128, schedule=2) == (128, 2, 2, 1, 2)
+    assert L(32, 4, 32, 32, 128, 128, schedule=3) == (128, 2, 1, 1, 3)      # the stream: one per CU
+    assert L(16, 2, 16, 16, 128, 128, schedule=3) == (128, 1, 1, 1, 3)      # ... and one group
+    assert L(1, 4, 8, 8, 128, 128, schedule=3) == (128, 1, 1, 1, 3)
+    # a caller's groups or cap take the AUTO stream back to the queue, which honours them
+    assert L(256, 4, 32, 32, 128, 128, column_groups=2) == (128, 2, 1, 2, 2)
+    assert L(256, 4, 32, 32, 128, 128, max_wg_per_cu=8) == (128, 2, 0, 1, 2)
+    assert L(256, 4, 32, 32, 128, 128, max_wg_per_cu=1) == (128, 2, 1, 1, 3)
     assert L(1, 4, 8, 8, 128, 128, schedule=2) == (128, 1, 0, 1, 2)          # the queue takes whole V
     assert L(8, 4, 16, 16, 128, 128, tile_columns=128) == (128, 1, 0, 1, 1)  # caller's tile: one group
     assert L(256, 4, 32, 32, 128, 128, tile_columns=128, schedule=2) == (128, 2, 0, 1, 2)
@@ -387,7 +413,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(64, 9, 8, 16, 128, 128, dtype="f32") == (64, 2, 1, 1, 1)
     assert L(512, 9, 32, 32, 128, 128, dtype="f32") == (64, 2, 1, 1, 1)
     assert kda.make_params(1, 0, 1, 1, 128, 128) and lib.kda_select_launch(
-        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None, None, None, None) == -2
+        ctypes.byref(kda.make_params(1, 0, 1, 1, 128, 128)), None, None, None, None, None, None, None) == -2
     # unit order: pairs for whole-V grids without a cap (every workgroup resident at once),
     # XCD ranges for capped grids, the 32-column split and the queue; the override wins
     O = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["unit_order"]
@@ -396,6 +422,7 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert O(32, 3, 32, 32, 128, 128) == 1                      # capped grid
     assert O(24, 4, 32, 32, 128, 128) == 2                      # uncapped grid of 768 units
     assert O(256, 4, 32, 32, 128, 128) == 1 and O(1, 4, 8, 8, 128, 128) == 1
+    assert O(256, 4, 32, 32, 128, 128, schedule=2) == 1
     assert O(2, 2, 2, 2, 16, 16) == 2                           # K = V = 16: whole V, no cap
     assert O(32, 4, 16, 16, 128, 128, unit_order=1) == 1 and O(256, 4, 32, 32, 128, 128, unit_order=2) == 2
     G = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["column_groups"]

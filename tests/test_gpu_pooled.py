@@ -99,11 +99,14 @@ def test_pooled_verify_matches_oracle(w, slots, pad, variant):
                                     dict(tile_columns=64, max_wg_per_cu=2),
                                     dict(tile_columns=128, max_wg_per_cu=1, column_groups=4),
                                     dict(tile_columns=128, max_wg_per_cu=1, schedule=2),
-                                    dict(tile_columns=128, max_wg_per_cu=1, column_groups=2, schedule=2)])
+                                    dict(tile_columns=128, max_wg_per_cu=1, column_groups=2, schedule=2),
+                                    dict(tile_columns=128, schedule=3, prefetch=1),
+                                    dict(tile_columns=128, schedule=3, prefetch=2)])
 def test_capped_grid_matches_oracle_and_uncapped(launch):
     """A workgroups-per-CU cap on a grid much larger than the part holds at once (padding
-    sequences among them), or the queue schedule pulling those units (padding units skip
-    and hand on their ticket), returns the bits of the uncapped grid and matches the oracle."""
+    sequences among them), or the queue or stream schedule pulling those units (padding
+    units skip and hand on their ticket; the stream's producer skips them without a load),
+    returns the bits of the uncapped grid and matches the oracle."""
     w = W(48, 3, 2, 8, gate="safe")  # 384 units of whole V: more than a persistent grid
     pinp, idx, init = _pooled_case(w, (60, 50, 70), seed=11, pad=(0, 17, 47))
     base, *_ = _run_pooled(w, pinp, idx, init, tile_columns=launch["tile_columns"])
@@ -164,8 +167,9 @@ def test_commit_matches_oracle_and_prefix_verify(w):
         assert torch.equal(d["conv_state"][idx["conv_state_indices"][n].item()], one["conv_state"][0]), n
 
 
-@pytest.mark.parametrize("launch", [dict(), dict(store_policy=2), dict(store_policy=2, schedule=2, max_wg_per_cu=1)],
-                         ids=["auto", "device-scope-stores", "device-scope-stores-queue"])
+@pytest.mark.parametrize("launch", [dict(), dict(store_policy=2), dict(store_policy=2, schedule=2, max_wg_per_cu=1),
+                                    dict(store_policy=2, schedule=3)],
+                         ids=["auto", "device-scope-stores", "device-scope-stores-queue", "device-scope-stores-stream"])
 def test_serving_loop_verify_commit_chain(launch):
     """Three rounds of verify -> commit on shared pools; each round's outputs match the
     oracle run on the pools the previous rounds left. Also with the snapshots streamed at

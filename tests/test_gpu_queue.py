@@ -86,14 +86,12 @@ def test_queue_with_fewer_units_than_resident_slots():
         assert_matches(w, o, oracle.verify_workload(w, inp), what="queue, 12 units")
 
 
-def test_auto_queue_on_the_large_batch_workload_matches_the_grid():
-    """The large-batch workload (N=256, T=4, H=HV=32) where AUTO picks the queue: identical
-    to the grid on every call, and every sequence matches the oracle."""
+def test_queue_on_the_large_batch_workload_matches_the_grid():
+    """The large-batch workload (N=256, T=4, H=HV=32) on the queue: identical to the grid on
+    every call, and every sequence matches the oracle."""
     w = synth.WORKLOADS["large_batch"]
-    p = kda.params_for(w)
-    assert kda.select_launch(p)["schedule"] == 2
     inp = synth.make_inputs(w)
-    queue = _chain(w, inp, 2)
+    queue = _chain(w, inp, 2, schedule=2)
     grid = _chain(w, inp, 1, schedule=1)[0]
     for q in queue:
         for k in OUTS:

@@ -171,13 +171,16 @@ STALE = [
     ("grid, 32-column split", dict(variant=kda.VARIANT_SMALL), "bytes"),
     ("queue", dict(schedule=2), "bytes"),
     ("queue", dict(schedule=2), "small"),
+    ("stream", dict(schedule=3), "bytes"),
+    ("stream", dict(schedule=3, prefetch=2), "small"),
 ]
 
 
 @pytest.mark.parametrize("what,launch,spoil", STALE, ids=[f"{c[0]}-{c[2]}" for c in STALE])
 def test_stale_counters_recovered_by_reset(what, launch, spoil):
     """Counters left non-zero (an interrupted call) may misplace the q/k conv_state write
-    and, on the queue, skip or repeat units; kda_workspace_reset restores correct results.
+    and, on the queue and the stream, skip or repeat units; kda_workspace_reset restores
+    correct results.
     The spoiled values are benign by construction (every byte 3, i.e. 0x03030303 in each
     counter, or small queue counts of 3 and 5): every ticket either names a unit in range
     or ends the loop, so the spoiled call cannot fault or hang (see kda_queue.h)."""
@@ -203,10 +206,11 @@ def test_stale_counters_recovered_by_reset(what, launch, spoil):
     assert_matches_all(w, inp, {**out, "conv_state": g["conv_state"]}, what=f"after reset, {what}")
 
 
-@pytest.mark.parametrize("qa", [0, 2])
+@pytest.mark.parametrize("qa", [0, 2, 3])
 def test_non_default_stream_and_concurrent_calls(qa):
-    """Overlapping calls on two streams with their own workspaces; with qa = 2 the first
-    runs the queue schedule over 2048 units while the second runs beside it."""
+    """Overlapping calls on two streams with their own workspaces; with qa = 2 (3, and AUTO
+    at 64 sequences) the first runs the queue (stream) schedule over 2048 units while the
+    second runs beside it."""
     wa = synth.WORKLOADS["gva"].with_(N=64 if qa else 6)
     wb = synth.WORKLOADS["small_batch"].with_(N=5, seed=77)
     say(f"[gpu] two streams, schedule {qa}")
@@ -231,7 +235,7 @@ def test_non_default_stream_and_concurrent_calls(qa):
     assert_matches(wb, {**ob, "conv_state": gb["conv_state"]}, oracle.verify_workload(wb, ib), what="stream b")
 
 
-@pytest.mark.parametrize("N,sched", [(8, 0), (64, 2)])
+@pytest.mark.parametrize("N,sched", [(8, 0), (64, 2), (64, 3)])
 def test_graph_replay_matches_eager(N, sched):
     """Capture one call in a HIP graph; every replay (conv_state restored eagerly in
     between) equals the eager result bit for bit. With the queue schedule (2048 units over

@@ -63,12 +63,14 @@ def test_unfused_close_to_fused_at_full_size():
 
 
 def test_unfused_rejects_the_queue_schedule():
-    """The unfused form keeps one workgroup per unit: an explicit queue is refused before
-    anything launches, and AUTO, which would pick the queue for the fused step, runs the grid."""
-    w = W(128, 4, 32, 32)  # 4096 units: AUTO's queue for the fused step
+    """The unfused form keeps one workgroup per unit: an explicit queue or stream is refused
+    before anything launches, and AUTO, which would pick the stream for the fused step, runs
+    the grid."""
+    w = W(128, 4, 32, 32)  # 4096 units: AUTO's stream for the fused step
     inp = synth.make_inputs(w)
-    with pytest.raises(kda.KdaError):
-        run_unfused(w, inp, schedule=2)
-    assert kda.select_launch(kda.params_for(w))["schedule"] == 2
+    for sched in (2, 3):
+        with pytest.raises(kda.KdaError):
+            run_unfused(w, inp, schedule=sched)
+    assert kda.select_launch(kda.params_for(w))["schedule"] == 3
     got = run_unfused(w, inp)
     assert_matches_all(w, inp, got, what="unfused, AUTO")
