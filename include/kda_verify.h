@@ -123,8 +123,8 @@ typedef struct {
   int32_t prefetch;         /* stream schedule only (ignored otherwise): when a workgroup
                                loads its next unit's state tile. 1 once the current unit's
                                conv phase is done; 2 as soon as the compute waves hold the
-                               current unit's state in registers. 0: 2 at T >= 3 up to
-                               65536 snapshot tiles (N * HV * T) per call, 1 otherwise */
+                               current unit's state in registers. 0: 2 up to 65536
+                               snapshot tiles (N * HV * T) per call, 1 beyond */
 } kda_verify_params;
 
 #define KDA_MAX_T 16

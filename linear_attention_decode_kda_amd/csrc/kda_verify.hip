@@ -918,7 +918,7 @@ __global__ __launch_bounds__(CF::NTHR) void kda_verify_queue_kernel(const Args a
 //   kPrefetchAtStart:    as soon as the compute waves hold the current unit's state in
 //                        registers (one more barrier), so that the state read overlaps the
 //                        conv phase as well. Measured faster up to 4 GiB of snapshots per call
-//                        at T >= 3 and slower beyond (the dispatch rule below).
+//                        and slower beyond (the dispatch rule below).
 // Loading it any later, in front of a token's snapshot stores, measured 4-20 % slower.
 enum StatePrefetch { kPrefetchAfterConv = 1, kPrefetchAtStart = 2 };
 
@@ -1407,13 +1407,12 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 //      (policy 1) at T = 2 and 4 and with four groups, device scope (policy 2) otherwise;
 //   3. T = 1, or < 1024 units, or < 2048 units at T = 2: the uncapped whole-V grid;
 //   4. < 2048 units at T = 3, 4: two whole-V workgroups per CU;
-//   5. otherwise the stream schedule (up to T = 8; the queue with two column groups at
-//      T = 2 and one beyond, above T = 8): the next unit's state loaded at the start of
-//      the current one at T >= 3 up to 65536 snapshot tiles of 64 KiB (4 GiB) per call,
-//      after its conv otherwise. Measured against the queue on 40 shapes of 1024-32768
-//      units, T = 2-8: +2-5 % up to 16384 units at T = 3-6 (large_batch +3.7 %, gva +3.5 %),
-//      +0.3-3 % on the larger calls with the later load, 1-2 % behind on two T = 8 shapes
-//      with shared q/k heads at 8192 units; below 2048 units it trails the grid buckets.
+//   5. otherwise the stream schedule (the queue above T = 8): the next unit's state loaded
+//      at the start of the current one up to 65536 snapshot tiles of 64 KiB (4 GiB) per
+//      call, after its conv beyond. On a third sweep (240 shapes of 1024-8192 units, T = 2-8,
+//      with both stream launches) the stream was the fastest launch on 169 shapes and the
+//      queue it replaced 4-7 % slower on average at T = 2-4; A/B runs on 40 shapes up to
+//      32768 units set the 4 GiB point (beyond it the later load was 0.3-3 % ahead).
 // Buckets 3-5 store at device scope. The unit order follows from the launch (choose_tile):
 // pairs for uncapped whole-V grids. Every launch uses the same K split (32 rows per wave)
 // and partial-sum tree, so all return bit-identical results; cap, schedule and order only
@@ -1435,7 +1434,7 @@ Tile auto_tile_128(long long units, int T) {
   if (T > 8) return Tile{128, kStoreNTDev, 1, 1, true};
   Tile t{128, kStoreNTDev, 1, 1};
   t.stream = true;
-  t.prefetch = T >= 3 && units * T <= 65536 ? kPrefetchAtStart : kPrefetchAfterConv;
+  t.prefetch = units * T <= 65536 ? kPrefetchAtStart : kPrefetchAfterConv;
   return t;
 }
 

@@ -113,6 +113,8 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
              "sets rotated so that >= 1 GiB is touched between reuses of a set. Launch names: `split32` the "
              "32-column split; `grid gG` whole-V workgroups without a cap in G column groups; `capC` at most C "
              "workgroups per CU (`64c`: 64 columns); `queue gG` one resident workgroup per CU pulling units; "
+             "`stream pP` the queue with a producer wave loading the next unit into LDS, its state tile after the "
+             "conv (p1) or at the start (p2); "
              "`s1` streaming stores, `s2` streaming at device scope; `o1` XCD-range unit order, `o2` pairs. "
              "Percent of the 8 TB/s HBM peak = algorithmic bytes / time (launch gap included). `rule` is the "
              "launch the library picks now; `rule/best` its time over the fastest launch.", "",

@@ -374,13 +374,13 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(1024, 16, 8, 8, 128, 128) == (128, 2, 1, 1, 2)
     assert L(128, 9, 8, 16, 128, 128) == (128, 2, 1, 1, 2)
     assert L(64, 8, 16, 32, 128, 128, dtype="f32") == (128, 2, 1, 1, 3)
-    # the stream's state prefetch: at the start at T >= 3 up to 65536 snapshot tiles per call,
-    # after the conv otherwise; the override wins
+    # the stream's state prefetch: at the start up to 65536 snapshot tiles per call, after the
+    # conv beyond; the override wins
     F = lambda *shape, **kw: kda.select_launch(kda.make_params(*shape, **kw))["prefetch"]
     assert F(64, 3, 16, 32, 128, 128) == 2 and F(256, 4, 32, 32, 128, 128) == 2
     assert F(256, 8, 32, 32, 128, 128) == 2                      # 65536 tiles
     assert F(512, 8, 16, 64, 128, 128) == 1 and F(512, 4, 16, 64, 128, 128) == 1
-    assert F(256, 2, 32, 32, 128, 128) == 1                      # T = 2
+    assert F(256, 2, 32, 32, 128, 128) == 2 and F(1024, 2, 64, 64, 128, 128) == 1   # T = 2
     assert F(256, 4, 32, 32, 128, 128, prefetch=1) == 1 and F(512, 8, 16, 64, 128, 128, prefetch=2) == 2
     assert F(32, 4, 16, 16, 128, 128) == 0 and F(1024, 16, 8, 8, 128, 128) == 0  # not the stream
     # overrides

@@ -42,7 +42,7 @@ CASES = [
     ((64, 4, 12, 24, "softplus"), (128, 2, 2, 1, 1)),   # 1536 units, T = 4: two per CU
     ((96, 1, 8, 24, "safe"), (128, 2, 0, 1, 1)),        # 2304 units, T = 1: the uncapped grid
     ((48, 3, 16, 48, "softplus"), (128, 2, 1, 1, 3)),   # 2304 units, T = 3: the stream, state at the start
-    ((96, 2, 12, 24, "safe"), (128, 2, 1, 1, 3)),       # 2304 units, T = 2: the stream, state after the conv
+    ((96, 2, 12, 24, "safe"), (128, 2, 1, 1, 3)),       # 2304 units, T = 2: the stream
     ((24, 6, 8, 48, "softplus"), (128, 2, 1, 1, 3)),    # 1152 units, T = 6: the stream from 1024 at T >= 5
     ((128, 9, 8, 16, "safe"), (128, 2, 1, 1, 2)),       # 2048 units, T = 9: the queue beyond T = 8
 ]
