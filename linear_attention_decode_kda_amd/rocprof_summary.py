@@ -117,7 +117,8 @@ def sweep_md(jsonl: str, cmd: str, out: str) -> None:
              "conv (p1) or at the start (p2); "
              "`s1` streaming stores, `s2` streaming at device scope; `o1` XCD-range unit order, `o2` pairs. "
              "Percent of the 8 TB/s HBM peak = algorithmic bytes / time (launch gap included). `rule` is the "
-             "launch the library picks now; `rule/best` its time over the fastest launch.", "",
+             "launch the library picks now; `rule/best` its time over the fastest launch (nan where this sweep did "
+             "not time that launch).", "",
              "| H | HV | T | N | units | fastest | % | AUTO at the time | rule now | rule % | rule/best |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     regs, per = [], {}
