@@ -37,3 +37,19 @@ def test_host_threads_bounds(monkeypatch):
     assert bench.host_threads() == 3
     monkeypatch.setenv("OMP_NUM_THREADS", "junk")
     assert 1 <= bench.host_threads() <= 16
+
+
+def test_sweep_launch_names_round_trip():
+    """Every launch the dispatch sweep times, given as overrides, is reported back by the
+    library's launch selection under the same name, so that a sweep table can find the
+    launch the rule picks among the timed ones (no GPU: host-only selection)."""
+    import linear_attention_decode_kda_amd as kda
+    launches = bench.sweep_launches()
+    assert "stream s2 p1" in launches and "stream s2 p2" in launches and len(launches) == 29
+    for name, kw in launches.items():
+        ln = kda.select_launch(kda.make_params(64, 4, 16, 32, 128, 128, **kw))
+        assert bench.launch_name(ln) == name, (name, ln)
+    # the rule's own picks on the named workloads carry sweep names too
+    for wl, want in (("small_batch", "grid g1 s1 o2"), ("gva", "stream s2 p2"), ("large_batch", "stream s2 p2"),
+                     ("max_bandwidth", "stream s2 p1")):
+        assert bench.launch_name(kda.select_launch(kda.params_for(synth.WORKLOADS[wl]))) == want, wl
