@@ -313,6 +313,10 @@ def make_pools(N: int, conv_state_indices=None, cache_indices=None, intermediate
     d.conv_state_slots = N if conv_state_slots is None else conv_state_slots
     d.state_slots = N if state_slots is None else state_slots
     d.intermediate_slots = N if intermediate_slots is None else intermediate_slots
+    # the descriptor holds the index tensors it points into, so that they live as long as it
+    # does (a temporary such as idx.cuda() would otherwise be freed, and its memory reused,
+    # before the call that reads it)
+    d.index_tensors = (conv_state_indices, cache_indices, intermediate_state_indices)
     return d
 
 

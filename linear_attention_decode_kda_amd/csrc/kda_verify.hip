@@ -1246,8 +1246,9 @@ __global__ __launch_bounds__(256) void kda_conv_silu_kernel(const ConvArgs a) {
 }
 
 // Accept step: one WG per (sequence, value head) copies the state snapshot of the last
-// accepted token into the state pool; the hv == 0 WG of the sequence also copies that
-// token's raw conv window into the conv cache pool. Pure 16-byte copies.
+// accepted token into the state pool, and one slice of that token's raw conv window into
+// the conv cache pool (the HV WGs of a sequence split the row between them). Pure 16-byte
+// copies.
 struct CommitArgs {
   const int32_t* accepted;
   const float* inter_ssm;
@@ -1263,7 +1264,11 @@ struct CommitArgs {
   int cs_vec;  // 16-byte vectors in one conv cache row (C * 3 elements)
 };
 
-__global__ __launch_bounds__(256) void kda_commit_kernel(const CommitArgs a) {
+// NT threads, U vectors per thread in each round, all loads of a round in flight before
+// its stores, which carry the streaming hint; the WG's slice of the conv row rides with the
+// first round. Two shapes, picked by the number of units in kda_verify_commit.
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void kda_commit_kernel(const CommitArgs a) {
   const int unit = xcd_order(blockIdx.x, gridDim.x), n = unit / a.HV, hv = unit % a.HV;
   const int acc = a.accepted[n];
   const int cs_row = a.cs_idx ? a.cs_idx[n] : n;
@@ -1272,33 +1277,33 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(const CommitArgs a) {
   if (acc < 1 || acc > a.T || cs_row < 0 || cs_row >= a.cs_slots || st_row < 0 || st_row >= a.st_slots ||
       in_row < 0 || in_row >= a.in_slots)
     return;
+  const int tid = threadIdx.x;
   const size_t src_tok = (size_t)in_row * a.T + (acc - 1);
   const f32x4* __restrict__ src = reinterpret_cast<const f32x4*>(a.inter_ssm) + (src_tok * a.HV + hv) * (size_t)a.kv4;
   f32x4* __restrict__ dst = reinterpret_cast<f32x4*>(a.state) + ((size_t)st_row * a.HV + hv) * (size_t)a.kv4;
-  // chunks of 8 vectors per thread: all loads of a chunk are in flight before its stores,
-  // which stream at device scope (nt sc1) like the snapshots: measured on MI355X against
-  // the streaming hint alone, 59.4 % of peak instead of 57.4-57.9 % for gva's commit,
-  // 71.3 % against 70.7 % for max_bandwidth's and 65.3 % against 64.9 % for large_batch's;
-  // plain stores lost 6-8 points
-  constexpr int U = 8;
-  for (int base = 0; base < a.kv4; base += U * 256) {
+  const u32x4* __restrict__ cw = reinterpret_cast<const u32x4*>(a.conv_window) + src_tok * (size_t)a.cs_vec;
+  u32x4* __restrict__ cs = reinterpret_cast<u32x4*>(a.conv_state) + (size_t)cs_row * a.cs_vec;
+  // this WG's vectors [c0, c1) of the conv row
+  const int per = (a.cs_vec + a.HV - 1) / a.HV;
+  const int c0 = min(a.cs_vec, hv * per), c1 = min(a.cs_vec, c0 + per);
+  for (int base = 0; base < a.kv4; base += U * NT) {
     f32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = base + u * 256 + (int)threadIdx.x;
+      const int i = base + u * NT + tid;
       if (i < a.kv4) v[u] = __builtin_nontemporal_load(src + i);
     }
+    const bool hc = base == 0 && c0 + tid < c1;
+    u32x4 c;
+    if (hc) c = cw[c0 + tid];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = base + u * 256 + (int)threadIdx.x;
-      if (i < a.kv4) store_snapshot<kStoreNTDev>(reinterpret_cast<float*>(dst + i), v[u]);
+      const int i = base + u * NT + tid;
+      if (i < a.kv4) store_snapshot<kStoreNT>(reinterpret_cast<float*>(dst + i), v[u]);
     }
+    if (hc) cs[c0 + tid] = c;
   }
-  if (hv == 0) {
-    const u32x4* __restrict__ cw = reinterpret_cast<const u32x4*>(a.conv_window) + src_tok * (size_t)a.cs_vec;
-    u32x4* __restrict__ cs = reinterpret_cast<u32x4*>(a.conv_state) + (size_t)cs_row * a.cs_vec;
-    for (int i = threadIdx.x; i < a.cs_vec; i += blockDim.x) cs[i] = cw[i];
-  }
+  for (int i = c0 + NT + tid; i < c1; i += NT) cs[i] = cw[i];
 }
 
 __global__ void zero_words(uint32_t* p, size_t n) {
@@ -1983,9 +1988,19 @@ kda_status kda_verify_commit(const kda_verify_params* p, const kda_pool_desc* po
   a.C = (int)C;
   a.kv4 = (int)(K * V / 4);
   a.cs_vec = (int)(C * 3 * s / 16);
+  // Up to 1024 units, 256 threads with 16 vectors each; beyond, 1024 threads with 4 each.
+  // Measured on MI355X against one 256-thread shape with 8 vectors per round, the whole
+  // conv row copied by the hv == 0 WG and device-scope streaming stores (cache evicted
+  // between calls): 29.7 -> 15.9 us at 512 units (small_batch), 66.7 -> 55.8 us at 2048
+  // (gva), 220 -> 191 us at 8192 (large_batch), 792 -> 725 us at 32768 (max_bandwidth); at
+  // 256-1024 units the small shape was 14-23 % ahead of the large one, from 2048 units the
+  // large one 6-9 % ahead of the small; device-scope stores lost 4-25 % on the small shape
+  // and were within 1.5 % either way on the large one.
+  const bool small = N * HV <= 1024;
+  const void* fn = small ? reinterpret_cast<const void*>(&kda_commit_kernel<256, 16>)
+                         : reinterpret_cast<const void*>(&kda_commit_kernel<1024, 4>);
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_commit_kernel), dim3((unsigned)(N * HV)), dim3(256),
-                         args, 0, stream) == hipSuccess
+  return hipLaunchKernel(fn, dim3((unsigned)(N * HV)), dim3(small ? 256 : 1024), args, 0, stream) == hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
 }

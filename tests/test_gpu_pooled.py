@@ -167,6 +167,40 @@ def test_commit_matches_oracle_and_prefix_verify(w):
         assert torch.equal(d["conv_state"][idx["conv_state_indices"][n].item()], one["conv_state"][0]), n
 
 
+@pytest.mark.parametrize("N,T,H,HV", [(32, 4, 16, 32), (41, 2, 1, 25), (40, 3, 8, 32)],
+                         ids=["1024-units", "1025-units-uneven-conv-slices", "1280-units"])
+def test_commit_both_kernel_shapes_match_oracle(N, T, H, HV):
+    """The accept step at unit counts on both sides of the switch between its two kernel
+    shapes (256 threads up to 1024 units, 1024 threads beyond), with the conv row split
+    unevenly over the value heads (25 of them), scattered pool rows, a padding row, and
+    sequences that accept nothing or every token: a bit copy, exact against the oracle, and
+    rows it must not write keep their bits."""
+    w = W(N, T, H, HV)
+    say(f"[gpu] commit {N}x{T}x{H}x{HV} ({N * HV} units)")
+    g = torch.Generator(device="cuda").manual_seed(21)
+    cg = torch.Generator().manual_seed(22)
+    slots = (N + 5, N + 3, N + 4)
+    cs_idx, st_idx, in_idx = (torch.randperm(s_, generator=cg)[:N].to(torch.int32) for s_ in slots)
+    st_idx[3] = -1  # padding sequence
+    acc = torch.tensor([n % (T + 1) for n in range(N)], dtype=torch.int32)  # 0 (nothing) .. T
+    inter = torch.randn((slots[2], T, HV, w.K, w.V), generator=g, device="cuda")
+    cw = torch.randn((slots[2], T, w.C, 3), generator=g, device="cuda").to(w.torch_dtype)
+    st = torch.randn((slots[1], HV, w.K, w.V), generator=g, device="cuda")
+    cs = torch.randn((slots[0], w.C, 3), generator=g, device="cuda").to(w.torch_dtype)
+    idx = {"conv_state_indices": cs_idx, "cache_indices": st_idx, "intermediate_state_indices": in_idx}
+    ref = oracle.commit(acc, idx, inter, cw, st, cs, T=T)
+    p = kda.params_for(w)
+    # index arrays made on the fly: the descriptor keeps them alive, so the allocations that
+    # follow (the accepted counts) cannot land in their memory
+    pools = kda.make_pools(N, cs_idx.cuda(), st_idx.cuda(), in_idx.cuda(), *slots)
+    assert [t.data_ptr() for t in pools.index_tensors] == [pools.conv_state_indices, pools.cache_indices,
+                                                            pools.intermediate_state_indices]
+    kda.verify_commit(p, pools, acc.cuda(), inter, cw, st, cs)
+    torch.cuda.synchronize()
+    assert torch.equal(st.cpu(), torch.from_numpy(ref["state"]).float())
+    assert np.array_equal(bits(cs), bits(torch.from_numpy(ref["conv_state"]).to(w.torch_dtype)))
+
+
 @pytest.mark.parametrize("launch", [dict(), dict(store_policy=2), dict(store_policy=2, schedule=2, max_wg_per_cu=1),
                                     dict(store_policy=2, schedule=3)],
                          ids=["auto", "device-scope-stores", "device-scope-stores-queue", "device-scope-stores-stream"])
