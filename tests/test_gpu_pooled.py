@@ -243,6 +243,78 @@ def test_serving_loop_verify_commit_chain(launch):
         assert np.abs(d["state"].cpu().numpy() - ref_st).max() <= TOL, rnd
 
 
+@pytest.mark.parametrize("sched", [0, 2, 3], ids=["auto", "queue", "stream"])
+def test_serving_step_graph_replay_matches_eager_chain(sched):
+    """One serving step (pooled verify, then commit) captured in a HIP graph and replayed for
+    three rounds, each round's inputs and accepted counts copied into the captured buffers
+    eagerly before its replay: after every replay the pools and outputs equal those of the
+    same three rounds run eagerly, bit for bit (the commit reads the verify's snapshots
+    inside one graph; on the queue and the stream each replay relies on the one before
+    having zeroed the counters)."""
+    w = W(24, 3, 4, 16, gate="safe")
+    slots = (28, 27, 26)
+    pinp, idx, init = _pooled_case(w, slots, seed=31)
+    di = {k: v.cuda() for k, v in idx.items()}
+    pools = kda.make_pools(w.N, di["conv_state_indices"], di["cache_indices"], di["intermediate_state_indices"],
+                           *slots)
+    p = kda.params_for(w, schedule=sched)
+    say(f"[gpu] serving-step graph {w.name} -> {kda.select_launch(p)}")
+    rounds = [synth.make_inputs(w, seed=200 + r) for r in range(3)]
+    accs = [torch.tensor([(n + r) % (w.T + 1) for n in range(w.N)], dtype=torch.int32) for r in range(3)]
+
+    def fresh_state():
+        d = {k: v.cuda() for k, v in pinp.items()}
+        return d, {k: v.cuda() for k, v in init.items()}, torch.zeros(w.N, dtype=torch.int32, device="cuda")
+
+    def step(d, out, acc, ws):
+        kda.kda_conv_verify_decode_pooled(p, pools, d["mixed_qkv"], d["conv_weight"], d["conv_state"], d["gate"],
+                                          d["A_log"], d["dt_bias"], d["beta"], d["state"], out["o"],
+                                          out["inter_ssm"], out["conv_window"], ws)
+        kda.verify_commit(p, pools, acc, out["inter_ssm"], out["conv_window"], d["state"], d["conv_state"])
+
+    def load_round(d, acc, r):
+        for k in ("mixed_qkv", "gate", "beta"):
+            d[k].copy_(rounds[r][k])
+        acc.copy_(accs[r])
+
+    def snap(d, out):
+        return {**{k: v.clone() for k, v in out.items()}, "state": d["state"].clone(),
+                "conv_state": d["conv_state"].clone()}
+
+    # eager chain
+    d, out, acc = fresh_state()
+    ws = kda.alloc_workspace(p)
+    eager = []
+    for r in range(3):
+        load_round(d, acc, r)
+        step(d, out, acc, ws)
+        torch.cuda.synchronize()
+        eager.append(snap(d, out))
+    # captured step, replayed over the same rounds from the same starting pools
+    d, out, acc = fresh_state()
+    ws = kda.alloc_workspace(p)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        load_round(d, acc, 0)
+        step(d, out, acc, ws)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    d, out, acc = fresh_state()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(d, out, acc, ws)
+    for r in range(3):
+        load_round(d, acc, r)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snap(d, out)
+        for k in got:
+            assert torch.equal(got[k], eager[r][k]), (r, k)
+    assert int(ws.count_nonzero().item()) == 0
+
+
 def test_pool_argument_errors():
     w = W(3, 2, 1, 2)
     p = kda.params_for(w)
