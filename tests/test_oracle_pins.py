@@ -220,6 +220,40 @@ def _small_inputs(N=2, T=3, H=2, HV=2, K=8, V=8, seed=0, dtype="f32", gate="soft
 
 
 @pytest.mark.parametrize("gate", ["softplus", "safe"])
+def test_zero_state_one_token_closed_form(gate):
+    """From a zero state, one token of the rule gives S_1 = beta k v^T (the decay acts on
+    zero and the prediction u is zero) and o = S_1^T q = beta (k . q) v. With identity conv
+    taps (tap 3 = 1, the rest 0) the activations are SiLU of the token itself, so q, k and v
+    come from the input channels through library routines alone: q = scale * normalize(
+    silu(x_q[h])), k = normalize(silu(x_k[h])), v = silu(x_v[hv]), h = hv // (HV / H). This
+    fixes which channels play q, k and v, and the head map, against the page's formula."""
+    w, inp = _small_inputs(N=2, T=1, H=2, HV=4, K=8, V=6, seed=3, gate=gate)
+    C = w.C
+    cw = torch.zeros(C, 4)
+    cw[:, 3] = 1.0
+    inp["conv_weight"] = cw
+    inp["state"] = torch.zeros_like(inp["state"])
+    scale = 0.3
+    out = oracle.verify(inp, H=w.H, HV=w.HV, K=w.K, V=w.V,
+                        gate_mode=oracle.GATE_SAFE if gate == "safe" else oracle.GATE_SOFTPLUS, scale=scale, eps=0.0)
+    x = torch.as_tensor(oracle.f64(inp["mixed_qkv"]))
+    act = F.silu(x)
+    beta = torch.sigmoid(torch.as_tensor(oracle.f64(inp["beta"])))
+    g = w.HV // w.H
+    for n in range(w.N):
+        for hv in range(w.HV):
+            h = hv // g
+            q = scale * F.normalize(act[n, 0, h * w.K:(h + 1) * w.K], dim=0)
+            k = F.normalize(act[n, 0, (w.H + h) * w.K:(w.H + h + 1) * w.K], dim=0)
+            v = act[n, 0, 2 * w.H * w.K + hv * w.V:2 * w.H * w.K + (hv + 1) * w.V]
+            b = beta[n, 0, hv]
+            np.testing.assert_allclose(out["inter_ssm"][n, 0, hv], (b * torch.outer(k, v)).numpy(), rtol=1e-12,
+                                       atol=1e-15)
+            np.testing.assert_allclose(out["o"][n, 0, hv], (b * torch.dot(k, q) * v).numpy(), rtol=1e-12,
+                                       atol=1e-15)
+
+
+@pytest.mark.parametrize("gate", ["softplus", "safe"])
 def test_beta0_alpha1_leaves_state(gate):
     """beta = 0 (raw -inf) and no decay (raw gate -inf): every snapshot equals the state,
     and o_t = state^T q_t with q_t from the conv + normalisation alone."""
