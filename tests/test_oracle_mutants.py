@@ -2,7 +2,9 @@
 
 Each case below copies the oracle package to a temporary folder with one plausible slip
 written into ``kda_oracle.c`` (a reversed tap order, an off-by-one window, a dropped scale,
-bias or exponential, a wrong sign, a q/k/v or head index mixed up, ...), builds that copy,
+bias or exponential, a wrong sign, a q/k/v or head index mixed up, ...) or into the pooled
+and accept-step functions of ``__init__.py`` (a pool row taken from the wrong index array,
+the wrong snapshot committed, padding not skipped), builds that copy,
 and runs ``tests/test_oracle_pins.py`` against it in a child process: at least one pin must
 fail. Two tests of that file do not count here, since they cannot tell a slip from the
 truth on their own: the stored tiny fixture (written by the oracle itself) and the torch
@@ -22,6 +24,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC_PATH = os.path.join(ROOT, "oracle", "kda_oracle.c")
+PY_PATH = os.path.join(ROOT, "oracle", "__init__.py")
 
 # (name, text in kda_oracle.c, text that replaces it)
 MUTANTS = [
@@ -70,6 +73,18 @@ MUTANTS = [
     ("gate-index-by-qk-head", "gate[nth * K + i]", "gate[(((size_t)n * T + t) * HV + h) * K + i]"),
 ]
 
+# the same, in the pooled and accept-step functions of oracle/__init__.py
+PY_MUTANTS = [
+    ("pooled-conv-row-by-sequence", '"conv_state": cs_pool[c:c + 1]', '"conv_state": cs_pool[n:n + 1]'),
+    ("pooled-state-row-by-sequence", '"state": st_pool[s_:s_ + 1]', '"state": st_pool[n:n + 1]'),
+    ("pooled-snapshot-row-by-cache-index", 'out_is[i] = r["inter_ssm"][0]', 'out_is[s_] = r["inter_ssm"][0]'),
+    ("pooled-window-row-by-conv-index", 'out_cw[i] = r["conv_window"][0]', 'out_cw[c] = r["conv_window"][0]'),
+    ("pooled-cache-not-written", 'cs_pool[c] = r["conv_state"][0]', 'pass'),
+    ("commit-wrong-token", "st[s_] = isp[i, a - 1]", "st[s_] = isp[i, a - 2]"),
+    ("commit-last-window", "cs[c] = cwp[i, a - 1]", "cs[c] = cwp[i, T - 1]"),
+    ("commit-accepts-zero", "if not (1 <= a <= T and", "if not (0 <= a <= T and"),
+]
+
 # Child process: load the copy as the module `oracle` before pytest imports anything, build
 # it, then run the pins. Exit 7 if the copy does not build.
 _DRIVER = r"""
@@ -92,13 +107,15 @@ sys.exit(pytest.main(["tests/test_oracle_pins.py", "-x", "-q", "-p", "no:cachepr
 """
 
 
-def _run_copy(source: str):
+def _run_copy(sources):
     d = tempfile.mkdtemp(prefix="kda_oracle_mutant_")
     try:
         os.makedirs(os.path.join(d, "oracle"))
-        shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), os.path.join(d, "oracle"))
+        c_src, py_src = sources
         with open(os.path.join(d, "oracle", "kda_oracle.c"), "w") as f:
-            f.write(source)
+            f.write(c_src)
+        with open(os.path.join(d, "oracle", "__init__.py"), "w") as f:
+            f.write(py_src)
         r = subprocess.run([sys.executable, "-c", _DRIVER, d], cwd=ROOT, capture_output=True, text=True,
                            timeout=600)
         caught = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED")]
@@ -109,11 +126,13 @@ def _run_copy(source: str):
 
 @pytest.fixture(scope="module")
 def results():
-    src = open(SRC_PATH).read()
-    jobs = {"control": src}
+    src, py = open(SRC_PATH).read(), open(PY_PATH).read()
+    jobs = {"control": (src, py)}
+    # each planted text must name exactly one place, so the lists follow the sources
     for name, old, new in MUTANTS:
-        # each planted text must name exactly one place, so the list follows the source
-        jobs[name] = src.replace(old, new) if src.count(old) == 1 else None
+        jobs[name] = (src.replace(old, new), py) if src.count(old) == 1 else None
+    for name, old, new in PY_MUTANTS:
+        jobs[name] = (src, py.replace(old, new)) if py.count(old) == 1 else None
     todo = {k: v for k, v in jobs.items() if v is not None}
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         done = dict(zip(todo, ex.map(_run_copy, todo.values())))
@@ -125,10 +144,10 @@ def test_unmodified_copy_passes_every_pin(results):
     assert rc == 0, info
 
 
-@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS + PY_MUTANTS])
 def test_planted_mistake_fails_a_pin(results, name):
     got = results[name]
-    assert got is not None, f"{name}: its text is not found exactly once in kda_oracle.c"
+    assert got is not None, f"{name}: its text is not found exactly once in the oracle source"
     rc, info = got
     assert rc != 7, f"{name}: the mutant copy did not build: {info}"
     assert rc == 1, f"{name}: no pin failed (exit {rc}): {info}"
