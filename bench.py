@@ -8,7 +8,10 @@ inputs already resident in HBM. Prints one JSON line:
   roofline   algorithmic HBM bytes per call / average kernel duration (HIP events on
              the launch stream), against the MI355X HBM peak of 8 TB/s
   cpu_baseline  the float64 oracle on bounded samples of the same workload, on all host
-                threads (sequence slices) and on one thread
+                threads (sequence slices) and on one thread; its `parity` compares one
+                fresh GPU call on the same inputs with the oracle on the multi-thread
+                sample (max |error| of o and inter_ssm against 2e-3, conv window and
+                rolled cache bit for bit)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large_batch]
 """
@@ -25,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+PARITY_TOL = 2e-3  # max |error| of o and inter_ssm the GPU parity tests accept
 
 
 def source_hash() -> str:
@@ -106,13 +110,17 @@ def host_description(threads: int) -> dict:
             "cpu_model": cpu_model()}
 
 
-def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
+def cpu_baseline(w, inp_cpu, budget_s: float, threads: int, gpu_out=None):
     """The oracle as it is (float64, sequential C) on bounded samples of the same inputs,
     run on slices of 4 sequences: (1) on one host thread over the first n sequences, n
     chosen from a one-slice probe to take about budget_s / 2; (2) on all `threads` host
     threads, each running the oracle on its own slices (ctypes releases the GIL), over as
-    many of the batch's sequences as fit in about budget_s / 2 (short samples repeated)."""
+    many of the batch's sequences as fit in about budget_s / 2 (short samples repeated).
+    With `gpu_out` (the device outputs of one call on these inputs, conv_state rolled in
+    place), one more untimed pass over sample (2) compares them with the oracle."""
     from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
 
     import oracle
     oracle.load()
@@ -150,6 +158,39 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
         t0 = time.perf_counter()
         done = sum(ex.map(run_slice, slices(n_mt, passes)))
         el_mt = time.perf_counter() - t0
+
+    parity = None
+    if gpu_out is not None:
+        import torch
+
+        def same_bits(got, ref64):
+            ref = torch.from_numpy(ref64).to(got.dtype)
+            iview = torch.int16 if got.element_size() == 2 else torch.int32
+            return bool(torch.equal(got.view(iview), ref.view(iview)))
+
+        def compare_slice(ab):
+            a, b = ab
+            part = {k: (v[a:b].contiguous() if k in per_seq else v) for k, v in inp_cpu.items()}
+            ref = oracle.verify_workload(w.with_(N=b - a), part)
+            e_o = float(np.abs(gpu_out["o"][a:b].double().cpu().numpy() - ref["o"]).max())
+            e_s = float(np.abs(gpu_out["inter_ssm"][a:b].cpu().numpy() - ref["inter_ssm"]).max())
+            return (e_o, e_s, same_bits(gpu_out["conv_window"][a:b].cpu(), ref["conv_window"]),
+                    same_bits(gpu_out["conv_state"][a:b].cpu(), ref["conv_state"]))
+
+        with ThreadPoolExecutor(threads) as ex:
+            res = list(ex.map(compare_slice, slices(n_mt)))
+        e_o = max(r[0] for r in res)
+        e_s = max(r[1] for r in res)
+        parity = {
+            "sequences": n_mt,
+            "o_max_abs_err": e_o,
+            "inter_ssm_max_abs_err": e_s,
+            "tolerance": PARITY_TOL,
+            "conv_window_bit_exact": all(r[2] for r in res),
+            "conv_state_bit_exact": all(r[3] for r in res),
+        }
+        parity["pass"] = bool(e_o <= PARITY_TOL and e_s <= PARITY_TOL and parity["conv_window_bit_exact"]
+                              and parity["conv_state_bit_exact"])
     return {
         "value": done * w.T / el_mt,
         "unit": "tokens/s",
@@ -161,6 +202,7 @@ def cpu_baseline(w, inp_cpu, budget_s: float, threads: int):
                   f"all T={w.T} tokens, same inputs, {passes} pass(es), in slices of {chunk} sequences over "
                   f"{threads} host threads; {el_mt:.1f} s",
         "single_thread": single,
+        "parity": parity,
     }
 
 
@@ -478,8 +520,20 @@ def main():
     copy_gbps = device_copy_gbps(b_alg, dev) if args.op == "verify" else None
     cpu = None
     if not args.no_cpu_baseline and args.op == "verify":
+        # one more call on a pristine copy of the inputs, for the parity readout
+        fresh = {k: v.to(dev) for k, v in inp_cpu.items()}
+        fresh_out = kda.alloc_outputs(w, dev)
+        kda.run(p, fresh, fresh_out, ws, stream)
+        torch.cuda.synchronize()
+        fresh_out["conv_state"] = fresh["conv_state"]
         print("[bench] timing the float64 oracle on a bounded sample (cpu_baseline)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, inp_cpu, args.cpu_budget, host_threads())
+        cpu = cpu_baseline(w, inp_cpu, args.cpu_budget, host_threads(), fresh_out)
+        del fresh, fresh_out
+        par = cpu["parity"]
+        print(f"[bench] parity on {par['sequences']} sequences: o {par['o_max_abs_err']:.2e}, inter_ssm "
+              f"{par['inter_ssm_max_abs_err']:.2e} (tolerance {PARITY_TOL}), conv window bits "
+              f"{par['conv_window_bit_exact']}, conv cache bits {par['conv_state_bit_exact']}", file=sys.stderr,
+              flush=True)
 
     line = {
         "metric": "verify tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",

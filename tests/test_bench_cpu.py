@@ -30,6 +30,38 @@ def test_cpu_baseline_legs_on_tiny_workload():
     assert cpu["cpu_model"] == bench.cpu_model() != ""
 
 
+def test_cpu_baseline_parity_readout():
+    """The parity readout of the CPU-baseline leg, fed the oracle's own outputs in their
+    stored dtypes (standing in for a GPU call): zero error and bit-exact conv outputs pass;
+    one snapshot element off by 1e-2 and one flipped conv-cache value each fail."""
+    import torch
+
+    import oracle
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w)
+    ref = oracle.verify_workload(w, inp)
+    dt = w.torch_dtype
+
+    def as_gpu():
+        return {"o": torch.from_numpy(ref["o"]).to(dt), "inter_ssm": torch.from_numpy(ref["inter_ssm"]).float(),
+                "conv_window": torch.from_numpy(ref["conv_window"]).to(dt),
+                "conv_state": torch.from_numpy(ref["conv_state"]).to(dt)}
+
+    par = bench.cpu_baseline(w, inp, 0.2, 2, as_gpu())["parity"]
+    json.dumps(par)
+    assert par["pass"] and par["sequences"] == w.N and par["tolerance"] == bench.PARITY_TOL
+    assert par["conv_window_bit_exact"] and par["conv_state_bit_exact"]
+    assert par["o_max_abs_err"] < 1e-6 and par["inter_ssm_max_abs_err"] < 1e-6
+    bad = as_gpu()
+    bad["inter_ssm"][1, 0, 1, 2, 3] += 1e-2
+    par = bench.cpu_baseline(w, inp, 0.2, 2, bad)["parity"]
+    assert not par["pass"] and par["inter_ssm_max_abs_err"] > bench.PARITY_TOL and par["conv_state_bit_exact"]
+    bad = as_gpu()
+    bad["conv_state"][0, 5, 1] = -bad["conv_state"][0, 5, 1] - 1
+    par = bench.cpu_baseline(w, inp, 0.2, 2, bad)["parity"]
+    assert not par["pass"] and not par["conv_state_bit_exact"] and par["conv_window_bit_exact"]
+
+
 def test_host_threads_bounds(monkeypatch):
     monkeypatch.setenv("OMP_NUM_THREADS", "64")
     assert bench.host_threads() == 16
