@@ -1108,16 +1108,24 @@ __device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>
       if (nd.valid) stream_stage_state<CF, R>(a, ss, nd, lane);
     }
     if (cur.valid) producer_barrier();  // B1: the compute waves are done with the staged inputs
-    if (drew) {
-      if (nd.valid) {
-        stream_stage_inputs<CF, R>(a, ss, nd, lane);
-        if (!state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane);
-      }
-      if (lane == 0) tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (drew && nd.valid) {
+      stream_stage_inputs<CF, R>(a, ss, nd, lane);
+      if (!state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane);
     }
+    // The ticket for the unit after nd is drawn at the last token's barrier, not here: near
+    // the end of the queue a unit drawn early waits in a workgroup that still has most of
+    // the current unit to run while others fall idle. The last token's update and stores
+    // still cover the atomic's round trip (measured on MI355X: 0.3-1.1 % faster on eight
+    // shapes, large_batch 417.1 -> 414.2 us).
     if (cur.valid) {
       producer_barrier();  // B2
-      for (int t = 0; t < a.T; ++t) producer_barrier();  // one per token
+      for (int t = 0; t < a.T; ++t) {
+        producer_barrier();  // one per token
+        if (t == a.T - 1 && drew && lane == 0)
+          tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (drew && lane == 0) {
+      tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (drew) {
