@@ -737,7 +737,7 @@ __device__ __forceinline__ void token_loop(const Args& a, Smem<CF, R>& s, f32x4 
 template <class CF, typename R, bool QUEUE>
 __device__ __forceinline__ void verify_unit(const Args& a, Smem<CF, R>& s, const int lb, const int slot) {
   constexpr int K = CF::K, V = CF::V, NCH = CF::NCH, E16 = CF::E16, NTHR = CF::NTHR;
-  constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR, M = CF::M;
+  constexpr int RPL = CF::RPL, VT = CF::VT, Q = CF::Q, LPR = CF::LPR;
 
   const int tid = threadIdx.x;
   // The ticket is drawn by thread 0 and read only by thread 0, on the same path, so no
