@@ -7,6 +7,7 @@ determinism stress (commit 2), multistream and graph replay, repeated chains
 (Tests & Accuracy), stale last-arrival counters (code review).
 """
 import ctypes
+import os
 
 import pytest
 import torch
@@ -28,9 +29,14 @@ def _setup(w, variant=kda.VARIANT_AUTO, **pkw):
     return inp, g, p, ws, out
 
 
-@pytest.mark.timeout(400)
+# repeats per workload; KDA_DET_ITERS raises it for a longer stress (the page's determinism
+# stress took its iteration count from a variable of that name)
+DET_ITERS = int(os.environ.get("KDA_DET_ITERS", "10000"))
+
+
+@pytest.mark.timeout(400 * max(1, -(-DET_ITERS // 10000)))
 @pytest.mark.parametrize("name", ["tiny", "small_batch", "gva", "large_batch", "max_bandwidth"])
-def test_determinism_repeats(name, reps=10000):
+def test_determinism_repeats(name, reps=DET_ITERS):
     """1e4 repeated calls on the same inputs give bitwise identical outputs, all of them on
     every repeat: o, every token's snapshot, every conv window and the rolled conv_state.
     conv_state is rolled in place, so it is restored from a pristine copy before each call.
