@@ -1114,26 +1114,36 @@ __device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>
     }
     // The ticket for the unit after nd is drawn at the last token's barrier, not here: near
     // the end of the queue a unit drawn early waits in a workgroup that still has most of
-    // the current unit to run while others fall idle. The last token's update and stores
-    // still cover the atomic's round trip (measured on MI355X: 0.3-1.1 % faster on eight
-    // shapes, large_batch 417.1 -> 414.2 us).
+    // the current unit to run while others fall idle. At that barrier the producer also
+    // counts nd into its q/k group (its loads landed long before) and reads the new unit's
+    // pool rows, so the last token's update and stores cover all three round trips and the
+    // hand-over only writes the descriptor (measured on MI355X: the late draw 0.3-1.1 %
+    // faster on eight shapes, large_batch 417.1 -> 414.2 us; the count-in moved with it
+    // another 0.3-0.9 % on shared q/k heads, gva 93.9 -> 93.1 us).
+    UnitDesc nn;  // the unit after nd
+    auto draw_and_count = [&]() {
+      if (drew) {
+        if (lane == 0) tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");  // nd's loads have landed; the ticket may fly
+        nd.last = stream_count_in(a, nd, CF::NVT, lane);
+        tk = (uint32_t)__builtin_amdgcn_readfirstlane((int)tk);
+        nn = stream_rows<CF>(a, kda_queue_unit(tk, units, G));
+      } else {
+        nn = stream_rows<CF>(a, -1);
+      }
+    };
     if (cur.valid) {
       producer_barrier();  // B2
       for (int t = 0; t < a.T; ++t) {
         producer_barrier();  // one per token
-        if (t == a.T - 1 && drew && lane == 0)
-          tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == a.T - 1) draw_and_count();
       }
-    } else if (drew && lane == 0) {
-      tk = __hip_atomic_fetch_add(qc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      draw_and_count();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (drew) {
-      tk = (uint32_t)__builtin_amdgcn_readfirstlane((int)tk);
-      nd.last = stream_count_in(a, nd, CF::NVT, lane);
-    }
     if (lane == 0) ss.desc[(it + 1) & 1] = nd;
-    nd = stream_rows<CF>(a, drew ? kda_queue_unit(tk, units, G) : -1);
+    nd = nn;
     producer_handover();
   }
   // every ticket this workgroup drew has been seen (the last one past the end): count out;
