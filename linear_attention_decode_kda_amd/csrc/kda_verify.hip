@@ -1056,15 +1056,16 @@ __device__ __forceinline__ void stream_stage_inputs(const Args& a, StreamSmem<CF
 }
 
 // Producer: issue the LDS-direct loads of a valid unit's state tile, 1 KiB per
-// instruction, with the streaming hint. Not waited for here.
+// instruction, with the streaming hint: instructions [j0, j1) of its 64. Not waited for
+// here.
 template <class CF, typename R>
 __device__ __forceinline__ void stream_stage_state(const Args& a, StreamSmem<CF, R>& ss, const UnitDesc& d,
-                                                   const int lane) {
+                                                   const int lane, const int j0 = 0, const int j1 = CF::K * CF::V / 256) {
   constexpr int K = CF::K, V = CF::V;
   const int hv = (d.lb / CF::NVT) % a.HV;
   const float* sp = a.state + ((size_t)d.st_row * a.HV + hv) * ((size_t)K * V) + lane * 4;
 #pragma unroll
-  for (int j = 0; j < K * V / 256; ++j)
+  for (int j = j0; j < j1; ++j)
     lds_direct<16, true>(sp + j * 256, reinterpret_cast<char*>(ss.st) + j * 1024);
 }
 
@@ -1117,9 +1118,14 @@ __device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>
     if (cur.lb < 0) break;
     const bool drew = nd.lb >= 0;
     const bool state_at_start = a.prefetch == kPrefetchAtStart && cur.valid;
+    // With the state loaded at the start, half of the next tile is issued at B0 and half
+    // after B1: the counter holds at most 63 loads, so issuing all 64 at B0 stalled the
+    // producer on the first one's return and could make it late for B1 (measured on
+    // MI355X: 0.2-1.1 % faster on seven of eight shapes, large_batch at T = 2 by 1.1 %;
+    // 48 or 56 first gained less, 16 first lost).
     if (state_at_start) {
       producer_barrier();  // B0: the compute waves hold the state tile in registers
-      if (nd.valid) stream_stage_state<CF, R>(a, ss, nd, lane);
+      if (nd.valid) stream_stage_state<CF, R>(a, ss, nd, lane, 0, 32);
     }
     if (it == 0 && count0) {
       prev0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev0);
@@ -1130,6 +1136,7 @@ __device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>
     }
     if (cur.valid) producer_barrier();  // B1: the compute waves are done with the staged inputs
     if (drew && nd.valid) {
+      if (state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane, 32, CF::K * CF::V / 256);  // the rest
       stream_stage_inputs<CF, R>(a, ss, nd, lane);
       if (!state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane);
     }
