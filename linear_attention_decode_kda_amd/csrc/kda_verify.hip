@@ -1135,11 +1135,29 @@ __device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     if (cur.valid) producer_barrier();  // B1: the compute waves are done with the staged inputs
-    if (drew && nd.valid) {
-      if (state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane, 32, CF::K * CF::V / 256);  // the rest
-      stream_stage_inputs<CF, R>(a, ss, nd, lane);
-      if (!state_at_start) stream_stage_state<CF, R>(a, ss, nd, lane);
+    const bool stage = drew && nd.valid;
+    if (stage) {
+      if (state_at_start) {
+        stream_stage_state<CF, R>(a, ss, nd, lane, 32, CF::K * CF::V / 256);  // the rest
+      } else {
+        stream_stage_inputs<CF, R>(a, ss, nd, lane);
+        stream_stage_state<CF, R>(a, ss, nd, lane, 0, 32);
+      }
     }
+    // after B2 (or at once for a padding unit): the inputs (state at the start) or the
+    // second half of the state tile (state after the conv). Issued together after B1,
+    // these loads outran the 63 the counter holds, and the producer came late to B2
+    // (measured on MI355X: large_batch 414.6 -> 410.5 us, gva 92.3 -> 91.2 us; within
+    // 0.3 % either way on the shapes it did not help).
+    auto stage_late = [&]() {
+      if (stage) {
+        if (state_at_start)
+          stream_stage_inputs<CF, R>(a, ss, nd, lane);
+        else
+          stream_stage_state<CF, R>(a, ss, nd, lane, 32, CF::K * CF::V / 256);
+      }
+    };
+    if (!cur.valid) stage_late();
     // The ticket for the unit after nd is drawn at the last token's barrier, not here: near
     // the end of the queue a unit drawn early waits in a workgroup that still has most of
     // the current unit to run while others fall idle. At that barrier the producer also
@@ -1162,6 +1180,7 @@ __device__ __forceinline__ void stream_producer(const Args& a, StreamSmem<CF, R>
     };
     if (cur.valid) {
       producer_barrier();  // B2
+      stage_late();
       for (int t = 0; t < a.T; ++t) {
         producer_barrier();  // one per token
         if (t == a.T - 1) draw_and_count();
