@@ -1475,8 +1475,8 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 //      one per CU, so 256 of them are one generation); one group at T = 1 beyond that, from
 //      448 units, and at odd T from 256 units; two groups otherwise. Streaming stores
 //      (policy 1) at T = 2 and 4 and with four groups, device scope (policy 2) otherwise;
-//   3. < 1024 units, or < 2048 units at T = 2, or < 3072 at T = 1: the uncapped whole-V grid;
-//   4. < 2048 units at T = 3, 4: two whole-V workgroups per CU;
+//   3. < 1024 units, or < 1280 units at T = 2, or < 3072 at T = 1: the uncapped whole-V grid;
+//   4. < 1280 units at T = 3, 4: two whole-V workgroups per CU;
 //   5. otherwise the stream schedule (the queue above T = 8): the next unit's state loaded
 //      at the start of the current one up to 65536 snapshot tiles of 64 KiB (4 GiB) per
 //      call, after its conv beyond. On a third sweep (240 shapes of 1024-8192 units, T = 2-8,
@@ -1484,7 +1484,12 @@ hipError_t launch(const Args& a, const Tile& tl, hipStream_t stream) {
 //      queue it replaced 4-7 % slower on average at T = 2-4; A/B runs on 40 shapes up to
 //      32768 units set the 4 GiB point (beyond it the later load was 0.3-3 % ahead); at T = 1
 //      a sweep of 70 shapes put the stream ahead of the grid from 3072 units (by 1-15 %, 88 %
-//      of the HBM peak at 32768 units) and behind it up to 2048.
+//      of the HBM peak at 32768 units) and behind it up to 2048. Once the stream's producer
+//      issued its loads spread over the unit's barriers and took its tickets at the last
+//      token, the sweeps, re-run, put the stream ahead at T = 2-4 from 1344 units, the first
+//      size above 1024 they hold (by 2.9-7.3 % on average per T and size), behind at 1024 (by
+//      3-10 %), and the grid still ahead at T = 1 up to 2048; buckets 3 and 4 now end at 1280
+//      units for T = 2-4, between those two sizes.
 // Buckets 3-5 store at device scope. The unit order follows from the launch (choose_tile):
 // pairs for uncapped whole-V grids. Every launch uses the same K split (32 rows per wave)
 // and partial-sum tree, so all return bit-identical results; cap, schedule and order only
@@ -1501,8 +1506,8 @@ Tile auto_tile_128(long long units, int T) {
       g = 2;
     return Tile{128, (T == 2 || T == 4 || g == 4) ? kStoreNT : kStoreNTDev, 0, g};
   }
-  if (units < 1024 || (units < 2048 && T == 2) || (units < 3072 && T == 1)) return Tile{128, kStoreNTDev};
-  if (units < 2048 && T <= 4) return Tile{128, kStoreNTDev, 2};
+  if (units < 1024 || (units < 1280 && T == 2) || (units < 3072 && T == 1)) return Tile{128, kStoreNTDev};
+  if (units < 1280 && T <= 4) return Tile{128, kStoreNTDev, 2};
   if (T > 8) return Tile{128, kStoreNTDev, 1, 1, true};
   Tile t{128, kStoreNTDev, 1, 1};
   t.stream = true;

@@ -355,18 +355,21 @@ def test_select_launch_follows_the_dispatch_rule(lib):
     assert L(8, 6, 16, 32, 128, 128) == (128, 2, 0, 2, 1)        # even T >= 6: device-scope stores
     assert L(16, 8, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(16, 2, 16, 16, 128, 128) == (128, 1, 0, 2, 1)       # T = 2 and 4: streaming stores
-    # 3. the uncapped grid: below 1024 units, below 2048 units at T = 2, below 3072 at T = 1
+    # 3. the uncapped grid: below 1024 units, below 1280 units at T = 2, below 3072 at T = 1
     assert L(24, 4, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(31, 8, 16, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(64, 1, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(95, 1, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
     assert L(96, 1, 32, 32, 128, 128) == (128, 2, 1, 1, 3)      # T = 1 from 3072 units: the stream
     assert L(512, 1, 16, 64, 128, 128) == (128, 2, 1, 1, 3)
-    assert L(63, 2, 32, 32, 128, 128) == (128, 2, 0, 1, 1)
-    # 4. two per CU below 2048 units at T = 3, 4
+    assert L(39, 2, 32, 32, 128, 128) == (128, 2, 0, 1, 1)       # 1248 units
+    assert L(40, 2, 32, 32, 128, 128) == (128, 2, 1, 1, 3)       # 1280 units: the stream
+    assert L(63, 2, 32, 32, 128, 128) == (128, 2, 1, 1, 3)
+    # 4. two per CU below 1280 units at T = 3, 4
     assert L(32, 3, 32, 32, 128, 128) == (128, 2, 2, 1, 1)
-    assert L(63, 4, 16, 32, 128, 128) == (128, 2, 2, 1, 1)
-    # 5. the stream, one per CU: from 2048 units at T = 2-4, from 1024 at T >= 5; the
+    assert L(39, 4, 16, 32, 128, 128) == (128, 2, 2, 1, 1)       # 1248 units
+    assert L(40, 4, 16, 32, 128, 128) == (128, 2, 1, 1, 3)       # 1280 units: the stream
+    # 5. the stream, one per CU: from 1280 units at T = 2-4, from 1024 at T >= 5; the
     # queue above T = 8
     assert L(64, 2, 16, 32, 128, 128) == (128, 2, 1, 1, 3)
     assert L(64, 3, 32, 32, 128, 128) == (128, 2, 1, 1, 3)

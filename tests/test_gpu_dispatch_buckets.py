@@ -1,9 +1,9 @@
 """Every branch of the dispatch rule on grids of 129-2304 (sequence, value head) units, on
 the GPU through the C ABI: one generation of whole-V workgroups in one, two or four column
 groups with either store policy (129-512 units), the uncapped grid below 1024 units; value-head counts that are not powers of
-two among them (HV = 12, 24, 36, 40, 48); two workgroups per CU below 2048 units at T = 3,
+two among them (HV = 12, 24, 36, 40, 48); two workgroups per CU below 1280 units at T = 3,
 4, the uncapped grid at T = 1 up to 3071 units, and the stream schedule (the queue beyond
-T = 8) from 2048 units at T = 2-4, from 1024 at T >= 5 and from 3072 at T = 1.
+T = 8) from 1280 units at T = 2-4, from 1024 at T >= 5 and from 3072 at T = 1.
 
 For each shape the launch AUTO picks is pinned, its results must equal those of the
 32-column split bit for bit (every launch shares the K split and the partial-sum tree),
@@ -39,7 +39,9 @@ CASES = [
     ((24, 3, 12, 36, "softplus"), (128, 2, 0, 1, 1)),   # 864 units, T = 3: the uncapped grid
     ((40, 4, 12, 24, "safe"), (128, 2, 0, 1, 1)),       # 960 units, T = 4: the uncapped grid
     ((9, 1, 32, 32, "softplus"), (128, 2, 0, 1, 1)),    # 288 units, T = 1: one group beyond 256
-    ((64, 4, 12, 24, "softplus"), (128, 2, 2, 1, 1)),   # 1536 units, T = 4: two per CU
+    ((48, 4, 12, 24, "softplus"), (128, 2, 2, 1, 1)),   # 1152 units, T = 4: two per CU
+    ((64, 4, 12, 24, "softplus"), (128, 2, 1, 1, 3)),   # 1536 units, T = 4: the stream from 1280
+    ((40, 2, 16, 32, "safe"), (128, 2, 1, 1, 3)),       # 1280 units, T = 2: the stream
     ((96, 1, 8, 24, "safe"), (128, 2, 0, 1, 1)),        # 2304 units, T = 1: the uncapped grid
     ((128, 1, 16, 32, "softplus"), (128, 2, 1, 1, 3)),  # 4096 units, T = 1: the stream from 3072
     ((48, 3, 16, 48, "softplus"), (128, 2, 1, 1, 3)),   # 2304 units, T = 3: the stream, state at the start
