@@ -10,19 +10,23 @@
 // Design (our own, for gfx950; the page's CuTe kernels target NVIDIA parts):
 //   * A unit of work is one (sequence n, value head hv, V-tile vt), done by one
 //     workgroup (WG) that holds the fp32 K x VT state tile in VGPRs for all T tokens.
-//     Two schedules: the grid (one WG per unit) and the queue (as many WGs as are
+//     Three schedules: the grid (one WG per unit); the queue (as many WGs as are
 //     resident at once, each pulling units from a counter in the workspace until none
-//     are left, so that no XCD idles while another still has units). The WG's NW
+//     are left, so that no XCD idles while another still has units); and the stream,
+//     the queue with a fifth wave per WG, the producer, that draws the tickets and loads
+//     the next unit's inputs and state tile straight into LDS while four compute waves
+//     run the current one (the compute waves then issue no vector-memory read; the AUTO
+//     choice for large batches). The WG's NW
 //     wave64s split K: wave w owns rows [w*RW, (w+1)*RW). Inside a wave, LPR = VT/4
 //     lanes span a row (one 16-byte vector of 4 columns each) and Q = 64/LPR
 //     consecutive rows are covered by one instruction, so every state load and
 //     snapshot store of a wave moves 64 x 16 contiguous bytes (two whole 512-byte rows
 //     when VT = 128).
-//   * Prologue: every input the WG needs besides the state (its q/k channels, its
-//     v-column channels, their conv cache and weights, the gate row, dt_bias, beta)
-//     is fetched with 16-byte loads into LDS; the 16-byte state loads are issued
-//     right behind them and stay in flight through the conv / gate / l2norm math,
-//     which all threads do from LDS.
+//   * Prologue (grid and queue): every input the WG needs besides the state (its q/k
+//     channels, its v-column channels, their conv cache and weights, the gate row,
+//     dt_bias, beta) is fetched with 16-byte loads into LDS; the 16-byte state loads are
+//     issued right behind them and stay in flight through the conv / gate / l2norm math,
+//     which all threads do from LDS. The stream's producer stages the same LDS layout.
 //   * Token loop: the decay is folded into the two K-reductions,
 //       u_j = sum_i (k_i a_i) S_ij,   w_j = sum_i (q_i a_i) S_ij,
 //       d_j = beta (v_j - u_j),       o_j = w_j + (q.k) d_j,
