@@ -1,4 +1,5 @@
-"""Compile the gfx950 HIP library in-tree: csrc/kda_verify.hip -> libkda_verify.so."""
+"""Compile the gfx950 HIP library in-tree: csrc/kda_verify.hip -> libkda_verify.so, and the
+plain C caller examples/verify_from_c.c -> examples/verify_from_c (linked to the library)."""
 from __future__ import annotations
 
 import os
@@ -12,6 +13,8 @@ HDR = os.path.join(ROOT, "include", "kda_verify.h")
 QHDR = os.path.join(PKG, "csrc", "kda_queue.h")
 LIB = os.path.join(PKG, "libkda_verify.so")
 ARCH = "gfx950"
+EXAMPLE_SRC = os.path.join(PKG, "examples", "verify_from_c.c")
+EXAMPLE = os.path.join(PKG, "examples", "verify_from_c")
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -46,6 +49,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_example(verbose: bool = False) -> str:
+    """The C caller, with gcc as C11 (the header must compile as C), linked to the library
+    found next to the package by a relative run path. Always recompiles."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = EXAMPLE + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{os.path.join(rocm, 'include')}", EXAMPLE_SRC, "-o", tmp,
+           f"-L{PKG}", "-lkda_verify", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed ({r.returncode}):\n{r.stderr}")
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
@@ -55,3 +76,4 @@ def is_stale() -> bool:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_example(verbose=True))
