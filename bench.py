@@ -349,7 +349,8 @@ def main():
                     help="seconds of untimed calls before the warm-up steps (clock and power ramp)")
     ap.add_argument("--workload", default="large_batch")
     ap.add_argument("--variant", default="auto", choices=["auto", "small", "large"])
-    ap.add_argument("--op", default="verify", choices=["verify", "verify_pooled", "commit", "unfused"],
+    ap.add_argument("--op", default="verify",
+                    choices=["verify", "verify_pooled", "commit", "unfused", "serve", "serve_no_commit"],
                     help="verify (the headline), verify on pooled buffers with scattered rows, the accept "
                          "step, or the unfused two-kernel form of verify (same algorithmic bytes)")
     ap.add_argument("--tile", type=int, default=0, help="override: V columns per workgroup (32, 64, 128)")
@@ -451,6 +452,42 @@ def main():
             kda.kda_conv_verify_decode_unfused(p, None, a["mixed_qkv"], a["conv_weight"], a["conv_state"],
                                                a["gate"], a["A_log"], a["dt_bias"], a["beta"], a["state"],
                                                o["o"], o["inter_ssm"], o["conv_window"], act, ws, stream)
+    elif args.op in ("serve", "serve_no_commit"):
+        # One serving step of a batch whose sequences all advance, sequence n accepting
+        # n % T + 1 tokens: with the accept step (verify on a state and a conv-cache pool,
+        # then commit into them), or without it (the verify reads each sequence's accepted
+        # snapshot row of the previous step's inter_ssm and conv_window, viewed as N*T state
+        # and conv-cache rows, and writes its own to a second set; the two sets alternate).
+        acc = (torch.arange(w.N, dtype=torch.int32) % w.T + 1).to(dev)
+        s_in = 2 if w.dtype == "bf16" else 4
+        if args.op == "serve":
+            ident = kda.make_pools(w.N)
+
+            def step():
+                kda.kda_conv_verify_decode_pooled(p, ident, inp["mixed_qkv"], inp["conv_weight"], inp["conv_state"],
+                                                  inp["gate"], inp["A_log"], inp["dt_bias"], inp["beta"], inp["state"],
+                                                  out["o"], out["inter_ssm"], out["conv_window"], ws, stream)
+                kda.verify_commit(p, ident, acc, out["inter_ssm"], out["conv_window"], inp["state"], inp["conv_state"],
+                                  stream)
+            b_alg = (synth.algorithmic_bytes(w) + w.N * (2 * 4 * w.HV * w.K * w.V + 2 * 3 * s_in * w.C)
+                     + 4 * 4 * w.N)
+        else:
+            NT = w.N * w.T
+            rows = torch.arange(w.N, dtype=torch.int32, device=dev) * w.T + acc - 1
+            snap_pools = kda.make_pools(w.N, rows, rows, None, NT, NT, w.N)
+            bufs = [out, kda.alloc_outputs(w, dev)]
+            kda.run(p, inp, bufs[1], ws)  # a first step from the inputs fills one set
+            par = [1]
+
+            def step():
+                prev, cur = bufs[par[0]], bufs[1 - par[0]]
+                par[0] = 1 - par[0]
+                kda.kda_conv_verify_decode_pooled(p, snap_pools, inp["mixed_qkv"], inp["conv_weight"],
+                                                  prev["conv_window"].view(NT, w.C, 3), inp["gate"], inp["A_log"],
+                                                  inp["dt_bias"], inp["beta"],
+                                                  prev["inter_ssm"].view(NT, w.HV, w.K, w.V), cur["o"],
+                                                  cur["inter_ssm"], cur["conv_window"], ws, stream)
+            b_alg = synth.algorithmic_bytes(w) + 2 * 4 * w.N
     else:
         # pools twice the batch, sequence rows scattered by a seeded permutation
         g = torch.Generator().manual_seed(w.seed)

@@ -203,7 +203,15 @@ kda_status kda_conv_verify_decode(const kda_verify_params* p, const void* mixed_
  * state pool, so sequences may share a state row there (a commit writes it: see
  * kda_verify_commit). The library does not read the device index arrays on the host, so
  * it cannot check distinctness: duplicated written rows race, and such a row ends up
- * holding an unspecified mix of the sequences' values. */
+ * holding an unspecified mix of the sequences' values.
+ * When every sequence of a batch advances every step, a call's snapshots can serve as the
+ * next call's pools, with no accept step in between: inter_ssm [P,T,HV,K,V] is also a
+ * state pool of P*T rows [HV,K,V], and conv_window [P,T,C,3] a conv_state pool of P*T
+ * rows [C,3], so cache_indices[n] = conv_state_indices[n] = r*T + a - 1 (r the sequence's
+ * intermediate row in the previous call, a its accepted tokens) starts sequence n from the
+ * accepted token's state and conv window. That call writes its own snapshots to a second
+ * pair of buffers (the two pairs alternate), and rolls the conv cache into the old
+ * conv_window row it read. The results are the bits of verify -> kda_verify_commit. */
 typedef struct {
   const int32_t* conv_state_indices;         /* row of conv_state [conv_state_slots, C, 3] */
   const int32_t* cache_indices;              /* row of state [state_slots, HV, K, V] */

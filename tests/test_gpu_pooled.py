@@ -356,3 +356,54 @@ def test_pool_argument_errors():
     pd = kda.make_pools(w.N)
     pd.conv_state_indices = out["o"].data_ptr()  # index array inside a written buffer
     assert raw(pd) == -7
+
+
+@pytest.mark.parametrize("w", [W(4, 4, 2, 4, gate="safe"), W(64, 4, 16, 32)], ids=["grid", "stream"])
+def test_commit_free_chain_equals_verify_commit_chain(w):
+    """A batch whose sequences all advance every step can skip the accept step: the next
+    verify takes its state rows from the previous step's inter_ssm viewed as N*T state rows
+    (row n*T + a_n - 1, the accepted token's snapshot) and its conv-cache rows from the
+    previous conv_window viewed the same way, and writes its own snapshots to a second set
+    of buffers (the two alternate). Over three steps with varying accepted counts this gives
+    the same bits as verify -> commit on a state and a conv-cache pool: o, inter_ssm and
+    conv_window of every step, and the state and conv cache each chain holds at the end.
+    The 64-sequence case runs on the stream (2048 units at T = 4)."""
+    p = kda.params_for(w)
+    ws = kda.alloc_workspace(p)
+    d = {k: v.cuda() for k, v in synth.make_inputs(w).items()}
+    ident = kda.make_pools(w.N)
+    st_a, cs_a = d["state"].clone(), d["conv_state"].clone()  # chain A: pools the commit updates
+    out_a = kda.alloc_outputs(w)
+    bufs = [kda.alloc_outputs(w), kda.alloc_outputs(w)]  # chain B: alternating snapshot sets
+    st_b, cs_b = d["state"].clone(), d["conv_state"].clone()
+    NT = w.N * w.T
+    seq = torch.arange(w.N, dtype=torch.int32, device="cuda")
+    acc = None
+    for step in range(3):
+        fresh = synth.make_inputs(w, seed=300 + step)
+        for k in ("mixed_qkv", "gate", "beta"):
+            d[k].copy_(fresh[k])
+        say(f"[gpu] commit-free chain {w.name} step {step}")
+        kda.kda_conv_verify_decode_pooled(p, ident, d["mixed_qkv"], d["conv_weight"], cs_a, d["gate"], d["A_log"],
+                                          d["dt_bias"], d["beta"], st_a, out_a["o"], out_a["inter_ssm"],
+                                          out_a["conv_window"], ws)
+        cur = bufs[step % 2]
+        if acc is None:
+            pools, cs_src, st_src = ident, cs_b, st_b
+        else:
+            prev = bufs[(step - 1) % 2]
+            rows = seq * w.T + acc - 1
+            pools = kda.make_pools(w.N, rows, rows, None, NT, NT, w.N)
+            cs_src, st_src = prev["conv_window"].view(NT, w.C, 3), prev["inter_ssm"].view(NT, w.HV, w.K, w.V)
+        kda.kda_conv_verify_decode_pooled(p, pools, d["mixed_qkv"], d["conv_weight"], cs_src, d["gate"], d["A_log"],
+                                          d["dt_bias"], d["beta"], st_src, cur["o"], cur["inter_ssm"],
+                                          cur["conv_window"], ws)
+        acc = torch.tensor([1 + (3 * n + step) % w.T for n in range(w.N)], dtype=torch.int32, device="cuda")
+        kda.verify_commit(p, ident, acc, out_a["inter_ssm"], out_a["conv_window"], st_a, cs_a)
+        torch.cuda.synchronize()
+        for k in ("o", "inter_ssm", "conv_window"):
+            assert np.array_equal(bits(out_a[k]), bits(cur[k])), (step, k)
+    last = bufs[2 % 2]
+    pick = (seq.long(), (acc - 1).long())
+    assert np.array_equal(bits(st_a), bits(last["inter_ssm"][pick])), "state after the last step"
+    assert np.array_equal(bits(cs_a), bits(last["conv_window"][pick])), "conv cache after the last step"
