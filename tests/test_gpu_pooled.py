@@ -407,3 +407,75 @@ def test_commit_free_chain_equals_verify_commit_chain(w):
     pick = (seq.long(), (acc - 1).long())
     assert np.array_equal(bits(st_a), bits(last["inter_ssm"][pick])), "state after the last step"
     assert np.array_equal(bits(cs_a), bits(last["conv_window"][pick])), "conv cache after the last step"
+
+
+@pytest.mark.parametrize("w", [W(6, 4, 2, 4, gate="safe"), W(64, 4, 16, 32)], ids=["grid", "stream"])
+def test_commit_free_step_graph_replay_matches_eager(w):
+    """The serving step without the accept step, captured as two HIP graphs (one per
+    direction between the two alternating snapshot sets) and replayed over four rounds, each
+    round's inputs and accepted-row indices copied into the captured buffers eagerly before
+    its replay: after every replay both snapshot sets equal those of the same rounds run
+    eagerly, bit for bit, and the workspace counters are back to zero."""
+    p = kda.params_for(w)
+    NT = w.N * w.T
+    base = synth.make_inputs(w)
+    rounds = [synth.make_inputs(w, seed=400 + r) for r in range(4)]
+    accs = [torch.tensor([1 + (5 * n + r) % w.T for n in range(w.N)], dtype=torch.int32) for r in range(4)]
+    say(f"[gpu] commit-free graph {w.name} -> {kda.select_launch(p)}")
+
+    def setup():
+        d = {k: v.cuda() for k, v in base.items()}
+        bufs = [kda.alloc_outputs(w), kda.alloc_outputs(w)]
+        rows = torch.zeros(w.N, dtype=torch.int32, device="cuda")
+        ws = kda.alloc_workspace(p)
+        kda.run(p, d, bufs[1], ws)  # the first step, from the initial state and conv cache
+        torch.cuda.synchronize()
+        return d, bufs, rows, ws
+
+    def load_round(d, rows, r):
+        for k in ("mixed_qkv", "gate", "beta"):
+            d[k].copy_(rounds[r][k])
+        rows.copy_(torch.arange(w.N, dtype=torch.int32) * w.T + accs[r] - 1)
+
+    def step(d, bufs, rows, ws, src):
+        prev, cur = bufs[src], bufs[1 - src]
+        pools = kda.make_pools(w.N, rows, rows, None, NT, NT, w.N)
+        kda.kda_conv_verify_decode_pooled(p, pools, d["mixed_qkv"], d["conv_weight"],
+                                          prev["conv_window"].view(NT, w.C, 3), d["gate"], d["A_log"], d["dt_bias"],
+                                          d["beta"], prev["inter_ssm"].view(NT, w.HV, w.K, w.V), cur["o"],
+                                          cur["inter_ssm"], cur["conv_window"], ws)
+
+    def snap(bufs):
+        return [{k: v.clone() for k, v in b.items()} for b in bufs]
+
+    d, bufs, rows, ws = setup()
+    eager = []
+    for r in range(4):  # round r reads set (r + 1) % 2 and writes the other
+        load_round(d, rows, r)
+        step(d, bufs, rows, ws, (r + 1) % 2)
+        torch.cuda.synchronize()
+        eager.append(snap(bufs))
+
+    d, bufs, rows, ws = setup()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        load_round(d, rows, 0)
+        step(d, bufs, rows, ws, 1)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    d, bufs, rows, ws = setup()
+    graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+    for src in (0, 1):
+        with torch.cuda.graph(graphs[src]):
+            step(d, bufs, rows, ws, src)
+    for r in range(4):
+        load_round(d, rows, r)
+        torch.cuda.synchronize()
+        graphs[(r + 1) % 2].replay()
+        torch.cuda.synchronize()
+        got = snap(bufs)
+        for i in (0, 1):
+            for k in got[i]:
+                assert torch.equal(got[i][k], eager[r][i][k]), (r, i, k)
+    assert int(ws.count_nonzero().item()) == 0
