@@ -12,7 +12,8 @@
  * kda_conv_verify_decode once on a stream of its own with a workspace it allocates and
  * zeroes with kda_workspace_reset, and writes o.bin, inter_ssm.bin, conv_window.bin and the
  * rolled cache conv_state_out.bin back to DIR. Every call is checked: a failed one prints
- * its status and the program exits 1.
+ * its status and the program exits 1; parameters the library rejects exit 2 before any
+ * file is read.
  */
 #include <stdio.h>
 #include <stdlib.h>
@@ -91,10 +92,20 @@ int main(int argc, char** argv) {
   const char* dir = argv[1];
   int v[8];
   for (int i = 0; i < 8; ++i) v[i] = atoi(argv[2 + i]);
+  if ((v[6] != 0 && v[6] != 1) || (v[7] != 0 && v[7] != 1)) {
+    fprintf(stderr, "DTYPE and GATE must be 0 or 1\n");
+    return 2;
+  }
   kda_verify_params p;
   kda_verify_params_init(&p, v[0], v[1], v[2], v[3], v[4], v[5]);
   p.in_dtype = v[6] ? KDA_BF16 : KDA_F32;
   p.gate_mode = v[7] ? KDA_GATE_SAFE : KDA_GATE_SOFTPLUS;
+  /* the library's own validation (host-only) before any size is formed from the shape */
+  const int32_t variant = kda_select_variant(&p);
+  if (variant < 0) {
+    fprintf(stderr, "invalid parameters: %s\n", kda_status_string(variant));
+    return 2;
+  }
 
   const size_t N = (size_t)p.N, T = (size_t)p.T, H = (size_t)p.H, HV = (size_t)p.HV, K = (size_t)p.K,
                V = (size_t)p.V;

@@ -34,13 +34,22 @@ def _args(w, d):
 
 
 def test_c_caller_is_built_and_checks_its_arguments(tmp_path):
-    """No GPU: the program is built, prints its usage on bad arguments and stops on a
-    missing input file before any HIP call."""
+    """No GPU: the program is built, prints its usage on bad arguments, rejects shapes and
+    flags the library's validation rejects, and stops on a missing input file before any HIP
+    call."""
     assert os.path.exists(kbuild.EXAMPLE), f"{kbuild.EXAMPLE} is not built; run __graft_entry__.build()"
     r = subprocess.run([kbuild.EXAMPLE], capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "usage" in r.stderr
     r = subprocess.run(_args(synth.WORKLOADS["tiny"], tmp_path), capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "cannot open" in r.stderr and "mixed_qkv.bin" in r.stderr
+    # shapes and flags the library rejects stop before any file is read
+    for bad in (synth.WORKLOADS["tiny"].with_(HV=3), synth.WORKLOADS["tiny"].with_(N=-1),
+                synth.WORKLOADS["tiny"].with_(K=8, V=8)):
+        r = subprocess.run(_args(bad, tmp_path), capture_output=True, text=True, timeout=60)
+        assert r.returncode == 2 and "invalid parameters" in r.stderr, (bad, r.stderr)
+    r = subprocess.run(_args(synth.WORKLOADS["tiny"], tmp_path)[:-1] + ["7"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 2 and "must be 0 or 1" in r.stderr
 
 
 @pytest.mark.gpu
