@@ -5,6 +5,8 @@ PR description: conv_state_indices, cache_indices and intermediate_state_indices
 normalised independently; per-token snapshots for rolling back to the accepted prefix.
 Tests & Accuracy: independent, non-contiguous state indices; repeated verify chains.
 """
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -479,3 +481,42 @@ def test_commit_free_step_graph_replay_matches_eager(w):
             for k in got[i]:
                 assert torch.equal(got[i][k], eager[r][i][k]), (r, i, k)
     assert int(ws.count_nonzero().item()) == 0
+
+
+def _random_pooled(seed=13, draws=30):
+    """Seeded random pooled cases: shape, pool sizes, padding entries and a schedule."""
+    rng, out = random.Random(seed), []
+    for i in range(draws):
+        K = rng.choice([16, 64, 128, 128])
+        H = rng.choice([1, 2, 4])
+        g = rng.choice([1, 2, 3])
+        T = rng.choice([1, 2, 3, 4, 6, 8])
+        N = rng.randint(1, 24)
+        dtype = rng.choice(["bf16", "bf16", "f32"])
+        gate = rng.choice(["softplus", "safe"])
+        w = W(N, T, H, H * g, K=K, V=K, dtype=dtype, gate=gate, seed=900 + i)
+        slots = tuple(N + rng.randint(0, 8) for _ in range(3))
+        pad = tuple(sorted(rng.sample(range(N), rng.randint(0, min(3, N - 1))))) if N > 1 else ()
+        kw = {}
+        if K == 128:
+            kw = rng.choice([{}, dict(schedule=2), dict(schedule=3), dict(schedule=3, prefetch=1),
+                             dict(schedule=1, tile_columns=32)])
+        out.append((w, slots, pad, kw))
+    return out
+
+
+RANDOM_POOLED = _random_pooled()
+
+
+@pytest.mark.parametrize("w,slots,pad,kw", RANDOM_POOLED,
+                         ids=[f"{c[0].name}-{c[0].dtype}-{c[0].gate}-slots{'x'.join(map(str, c[1]))}-pad{len(c[2])}"
+                              f"-{'-'.join(f'{k}{v}' for k, v in c[3].items()) or 'auto'}" for c in RANDOM_POOLED])
+def test_random_pooled_shapes_match_oracle(w, slots, pad, kw):
+    """Seeded random shapes on pools larger than the batch, rows picked at random, up to
+    three padding entries, on the AUTO launch, the queue, the stream (either prefetch point)
+    or 32-column grid tiles; every output against the oracle's pooled step (padding rows of
+    o left as they were, conv bits exact)."""
+    pinp, idx, init = _pooled_case(w, slots, seed=w.seed, pad=pad)
+    got, *_ = _run_pooled(w, pinp, idx, init, **kw)
+    ref = oracle.verify_pooled(pinp, {**idx, **init}, H=w.H, HV=w.HV, K=w.K, V=w.V, gate_mode=_gm(w))
+    _compare(w, got, ref)
